@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse NVFP4 MLA decode hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of the workload: for the
+default workload (35 decode tokens x 16 heads, 2,048-entry index lists over a
+262,144-row NVFP4 pool) that is one sparse_mla_decode launch (gather, on-chip
+unpack, QK^T, online softmax, PV and the in-launch log-sum-exp combine); the
+throughput workload (--config 5) also writes its 1,024 new rows with
+nvfp4_pack_rows first.  Inputs are resident in HBM before timing starts.
+
+Cold caches without a flush in the timed region: every step attends a different
+"layer" -- one of L copies of the pool, L chosen so the copies span >= 2 GiB --
+so a step never finds its rows in the 256 MB Infinity Cache left by the steps
+before it (as in serving, where the other layers run between two launches of one
+layer).
+
+Prints one JSON line on stdout.  `value` is decode tokens per second of the
+whole step; `roofline` prices the decode kernel's gathered KV bytes (352 bytes
+per valid list entry) against its average launch duration measured with HIP
+events around each launch on the launch stream; `cpu_baseline` times the CPU
+oracle on the host on the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16 matrix, published
+ROW_BYTES = 352
+COLD_SPAN_BYTES = 2 << 30      # layer copies span at least this much
+METRIC = "sparse NVFP4 MLA decode: µs/launch, tokens/s, achieved HBM GB/s vs peak"
+KERNEL_SOURCES = ["sparse_mla_decode_04_amd/csrc/decode.hip", "sparse_mla_decode_04_amd/csrc/smla_device.hpp",
+                  "sparse_mla_decode_04_amd/csrc/smla_combine.hpp", "sparse_mla_decode_04_amd/csrc/smla_decode.hpp",
+                  "sparse_mla_decode_04_amd/csrc/api.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per decode launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, q, idx, src, seconds):
+    """Time the oracle on the host over the workload's tokens (repeating the token list
+    until about `seconds` have passed).  The oracle's rows are quantized beforehand by the
+    oracle's own row writer (untimed), so the timed part is what one GPU launch does:
+    gather, dequant, attention."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    ids = np.unique(idx[idx >= 0])
+    rows = np.zeros((wl.pool_rows, ROW_BYTES), dtype=np.uint8)
+    rows[ids] = oracle.nvfp4_pack_rows_ref(src[ids])
+    tokens_done = 0
+    t0 = time.perf_counter()
+    while True:
+        for t in range(wl.T):
+            oracle.sparse_mla_decode_ref(q, rows, idx, wl.softmax_scale, tokens=[t])
+            tokens_done += 1
+            if time.perf_counter() - t0 >= seconds and tokens_done >= 1:
+                break
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens_done / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"{tokens_done} decode tokens of the {wl.name} workload (the {wl.T}-token batch "
+                      f"repeated), float64 numpy oracle, {dt:.1f} s; elementwise work single-threaded, "
+                      f"BLAS with {blas} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, the 35-token launch)")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget, 0 disables")
+    ap.add_argument("--check-tokens", type=int, default=3, help="tokens checked against the oracle (untimed)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus}, WORLD_SIZE {world}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_mla_decode_04_amd as smla
+    from sparse_mla_decode_04_amd import binding, workloads as W
+    from helpers import OracleRows, build_device_pool, parity_errors, pool_source_all
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    smla.lib()
+    dev = "cuda"
+    wl = W.WORKLOADS[args.config]
+    log(f"workload {wl.name}: T={wl.T} H={wl.H} pool_rows={wl.pool_rows} topk={wl.topk}")
+
+    t_setup = time.time()
+    src_full = pool_source_all(wl)            # with the workload's new rows at their slots
+    new, slots = W.new_rows(wl)
+    src_base = src_full
+    if len(slots):                            # the step writes them; start from the base pool
+        src_base = np.concatenate([c for _, c in W.pool_source_chunks(wl)], axis=0)
+    pool0 = build_device_pool(src_base, dev)
+    pool_bytes = pool0.numel()
+    L = max(2, -(-COLD_SPAN_BYTES // pool_bytes))
+    layers = [pool0] + [pool0.clone() for _ in range(L - 1)]
+    q = W.queries(wl)
+    idx = W.index_lists(wl)
+    q_d = torch.from_numpy(q).to(dev)
+    idx_d = torch.from_numpy(idx).to(dev)
+    out = torch.empty((wl.T, wl.H, 512), dtype=torch.float16, device=dev)
+    lse = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+    ws = smla.make_workspace(wl.T, wl.H, wl.topk, args.num_splits, dev)
+    decode = [binding.prepare_decode(q_d, p, idx_d, wl.softmax_scale, out, lse, args.num_splits, ws) for p in layers]
+    pack = []
+    if len(slots):
+        new_d = torch.from_numpy(new).to(dev)
+        slots_d = torch.from_numpy(slots).to(dev)
+        pack = [binding.prepare_pack(new_d, slots_d, p) for p in layers]
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s; {L} layer copies of {pool_bytes / 1e6:.1f} MB; "
+        f"splits {smla.choose_num_splits(wl.T, wl.H, wl.topk) if args.num_splits == 0 else args.num_splits}")
+
+    n_valid = int(np.sum((idx >= 0) & (idx < wl.pool_rows)))
+    kv_bytes = n_valid * ROW_BYTES
+
+    def step(i, ev=None):
+        l = i % L
+        if pack:
+            pack[l]()
+        if ev is not None:
+            ev[0].record()
+        decode[l]()
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # untimed parity check of the last step's output against the oracle
+    if args.check_tokens > 0:
+        import oracle
+        rng = np.random.default_rng(0)
+        toks = sorted(rng.choice(wl.T, size=min(wl.T, args.check_tokens), replace=False).tolist())
+        ref_o, ref_l = oracle.sparse_mla_decode_ref(q, OracleRows(src_full), idx, wl.softmax_scale, tokens=toks)
+        oe, le, ok = parity_errors(out.cpu().numpy()[toks], lse.cpu().numpy()[toks], ref_o, ref_l)
+        log(f"parity on tokens {toks}: out err {oe:.2e} (tol 2e-3), lse err {le:.2e} (tol 1e-3), -inf ok {ok}")
+        if not (oe <= 2e-3 and le <= 1e-3 and ok):
+            print("bench.py: output does not match the oracle", file=sys.stderr)
+            sys.exit(3)
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kms = np.array([a.elapsed_time(b) for a, b in evs])
+    k_avg = float(np.mean(kms))
+    achieved = kv_bytes / (k_avg * 1e-3) / 1e9
+    log(f"decode launch: mean {k_avg * 1e3:.2f} us, median {np.median(kms) * 1e3:.2f} us, "
+        f"min {np.min(kms) * 1e3:.2f} us; step {ms_per_step * 1e3:.2f} us; "
+        f"gathered KV {kv_bytes / 1e6:.2f} MB -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    traffic = traffic_from_profiles(wl.name)
+    flops = 2.0 * wl.H * (576 + 512) * n_valid        # QK^T over 576 + PV over 512, per valid entry
+    tflops = flops / (k_avg * 1e-3) / 1e12
+    if flops / kv_bytes > MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):   # above the ridge
+        roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": tflops / MFMA_F16_PEAK_TFS, "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+    log(f"matrix work {flops / 1e9:.2f} GFLOP -> {tflops:.1f} TFLOP/s ({tflops / MFMA_F16_PEAK_TFS:.1%} of 2.5 PF)")
+    res = {
+        "metric": METRIC,
+        "value": wl.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "decode_tokens": wl.T, "heads": wl.H, "topk": wl.topk,
+                   "pool_rows": wl.pool_rows, "valid_entries": n_valid, "row_bytes": ROW_BYTES,
+                   "cache_write_rows": int(len(slots)), "layer_copies": L,
+                   "num_splits": args.num_splits or smla.choose_num_splits(wl.T, wl.H, wl.topk),
+                   "us_per_launch": k_avg * 1e3},
+        "roofline": roof,
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, q, idx, src_full, args.cpu_seconds)
+        log(f"cpu oracle: {res['cpu_baseline']['value']:.1f} tokens/s")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * smla.h -- C ABI of the sparse NVFP4 multi-head-latent-attention decode library
+ * (libsmla.so, HIP kernels for AMD gfx950 / MI355X).
+ *
+ * The method: "Prime Intellect Launches Prime Inference, Serving 600B Tokens Daily",
+ * section "Four-bit caches make room".  The MLA KV cache is stored as NVFP4 (four-bit
+ * values with one FP8 scale per group of 16), which shrinks a cache row from 576 to
+ * 352 bytes; the native sparse-attention kernel loads only the rows the sparse indexer
+ * selected, unpacks them on chip, runs attention with FP16 operands and FP32
+ * accumulation, handles the empty entries of the 2,048-position index list, and sizes
+ * its work decomposition by the token batch.  A staged variant first unpacks NVFP4 into
+ * FP8 buffers and then runs attention.
+ *
+ * Cache row (SMLA_ROW_BYTES = 352 bytes), one per cached token:
+ *   bytes [0, 256)    512 latent values as E2M1 codes; element 2i in bits 3:0 and
+ *                     element 2i+1 in bits 7:4 of byte i
+ *   bytes [256, 288)  32 FP8 E4M3 (OCP "FN") scales; byte 256+j scales elements 16j..16j+15
+ *   bytes [288, 352)  64 rope values as FP8 E4M3
+ * A latent value is E2M1(code) * E4M3(scale); a rope value is E4M3(code).  Both are
+ * exact in fp16.  The query of a head has 576 fp16 values: the first 512 pair with the
+ * latent, the last 64 with the rope part; the attention output is the 512-wide latent.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device memory owned by the caller; the library never
+ *     allocates, frees or synchronizes.  Arrays are dense, row-major, and must be
+ *     16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only enqueued;
+ *     completion is observed by the caller (event or stream synchronize).
+ *   - Return value: SMLA_OK or a negative smla_status.  Arguments are checked on the
+ *     host before anything is enqueued; on error nothing is enqueued.  No C++
+ *     exception crosses this interface.
+ *   - Index lists: int32, -1 (any negative value) marks an empty entry.  An entry
+ *     >= pool_rows is treated as empty as well, so no list entry can make a kernel read
+ *     outside the pool.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SMLA_API __attribute__((visibility("default")))
+#else
+#define SMLA_API
+#endif
+
+#define SMLA_ROW_BYTES 352
+#define SMLA_HEAD_DIM 576
+#define SMLA_LATENT_DIM 512
+#define SMLA_ROPE_DIM 64
+#define SMLA_GROUP 16
+
+typedef enum {
+  SMLA_OK = 0,
+  SMLA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misalignment */
+  SMLA_ERR_UNSUPPORTED = -2,   /* a shape the kernels do not handle (e.g. H not a multiple of 16) */
+  SMLA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+  SMLA_ERR_LAUNCH = -4,        /* the HIP runtime rejected a kernel launch */
+} smla_status;
+
+/* Human-readable name of a status code (static string). */
+SMLA_API const char* smla_status_string(int status);
+
+/*
+ * Row codec, cache write ("Four-bit caches make room": NVFP4 stays the storage format).
+ * Quantizes n fp16 rows src_dev[n][576] and writes each as a 352-byte cache row at
+ * kv_pool_dev + slots_dev[i] * 352.  Per group of 16 latent values: scale = E4M3 nearest
+ * to amax/6 (ties to even, saturating at 448); code = E2M1 nearest to x/scale (ties to
+ * even, saturating at 6, sign kept; a zero scale gives signed zeros).  Rope values:
+ * E4M3 nearest (ties to even, saturating at 448).  Rows whose slot is negative or
+ * >= pool_rows are skipped.  Inputs must be finite.  Slots must be distinct (two rows
+ * written to one slot race).  n == 0 enqueues nothing.
+ */
+SMLA_API int nvfp4_pack_rows(const void* src_dev, const int32_t* slots_dev, int32_t n,
+                    void* kv_pool_dev, int64_t pool_rows, void* stream);
+
+/*
+ * Test / inspection export of the on-chip unpack used by the decode kernels.
+ * Decodes the cache rows rows_dev[i] (i < n) to fp16 out_dev[n][576], bit-exact
+ * (latent = E2M1 * E4M3 scale, rope = E4M3).  A row id that is negative or >= pool_rows
+ * gives a zero row.
+ */
+SMLA_API int nvfp4_unpack_rows_f16(const void* kv_pool_dev, int64_t pool_rows, const int32_t* rows_dev,
+                          int32_t n, void* out_dev, void* stream);
+
+/*
+ * Sparse MLA decode ("Four-bit caches make room": loads only the selected rows, unpacks
+ * on chip, FP16 operands with FP32 accumulation, empty list entries handled).
+ *   q_dev        fp16 [T][H][576]
+ *   kv_pool_dev  uint8 [pool_rows][352] cache rows
+ *   indices_dev  int32 [T][topk] row ids, -1 = empty
+ *   out_dev      fp16 [T][H][512]:  sum_j softmax_j * latent_j over the valid entries
+ *   lse_dev      fp32 [T][H]:       ln sum_j exp(softmax_scale * q.k_j)
+ * An entry list with no valid entry gives out = 0 and lse = -inf.  Repeated rows count
+ * once per entry.  H must be a multiple of 16; 1 <= topk <= 65536.
+ *   num_splits   0 = automatic.  Otherwise the number of workgroups per 16-head group
+ *                that share the T*ceil(topk/64) row chunks (clamped to that count).
+ *   workspace    device scratch of at least smla_decode_workspace_bytes(T, H, topk,
+ *                num_splits) bytes, zero-filled before its first use.  Every call
+ *                leaves the counters it uses at zero again, so a workspace can be
+ *                reused by later calls on the same stream without clearing; calls that
+ *                run concurrently must not share one.  May be NULL if that size is 0.
+ * The partial results of the workgroups that share a token are merged inside the same
+ * launch by the workgroup that finishes last (log-sum-exp combine).
+ */
+SMLA_API int sparse_mla_decode(const void* q_dev, const void* kv_pool_dev, int64_t pool_rows,
+                      const int32_t* indices_dev, int32_t T, int32_t H, int32_t topk,
+                      float softmax_scale, void* out_dev, float* lse_dev, int32_t num_splits,
+                      void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* The split count the automatic mode of sparse_mla_decode uses for this shape. */
+SMLA_API int32_t smla_choose_num_splits(int32_t T, int32_t H, int32_t topk);
+
+/* Workspace bytes sparse_mla_decode needs (num_splits as passed to it, 0 = automatic). */
+SMLA_API size_t smla_decode_workspace_bytes(int32_t T, int32_t H, int32_t topk, int32_t num_splits);
+
+/*
+ * Log-sum-exp combine of split results (the merge step of the split work above).
+ *   partial_out_dev  fp32 [T][S][H][512]  normalized output of each split
+ *   partial_lse_dev  fp32 [T][S][H]       natural-log LSE of each split (-inf = empty split)
+ *   out_dev fp16 [T][H][512], lse_dev fp32 [T][H]:
+ *       lse = ln sum_s exp(lse_s);  out = sum_s exp(lse_s - lse) * out_s
+ * Splits with lse_s = -inf weigh zero; if all are -inf, out = 0 and lse = -inf.
+ */
+SMLA_API int sparse_mla_combine(const float* partial_out_dev, const float* partial_lse_dev, int32_t T,
+                       int32_t S, int32_t H, void* out_dev, float* lse_dev, void* stream);
+
+/*
+ * Staged variant, pass 1 ("Four-bit caches make room": the staged implementation first
+ * unpacked NVFP4 values into FP8 buffers).  For every list entry (t, j) writes the 576
+ * values of row indices_dev[t][j], re-encoded as FP8 E4M3 (nearest, ties to even,
+ * saturating at 448), to staged_dev + (t*topk + j)*576; an empty entry writes 576 zero
+ * bytes.  staged_dev holds T*topk*576 bytes.
+ */
+SMLA_API int nvfp4_stage_fp8(const void* kv_pool_dev, int64_t pool_rows, const int32_t* indices_dev,
+                    int32_t T, int32_t topk, void* staged_dev, void* stream);
+
+/*
+ * Staged variant, pass 2: attention over the FP8 rows written by nvfp4_stage_fp8
+ * (E4M3 -> fp16 exactly, FP16 operands, FP32 accumulation).  indices_dev only marks
+ * which entries are empty.  Arguments otherwise as in sparse_mla_decode, with
+ * smla_decode_workspace_bytes giving the workspace size.
+ */
+SMLA_API int sparse_mla_decode_fp8rows(const void* q_dev, const void* staged_dev,
+                              const int32_t* indices_dev, int64_t pool_rows, int32_t T, int32_t H,
+                              int32_t topk, float softmax_scale, void* out_dev, float* lse_dev,
+                              int32_t num_splits, void* workspace_dev, size_t workspace_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

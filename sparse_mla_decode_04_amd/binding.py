@@ -1,0 +1,240 @@
+"""ctypes binding of libsmla.so (include/smla.h).
+
+Argument marshalling only: every function checks the torch tensors it is handed
+(device, dtype, shape, contiguity), passes their device pointers and the current
+HIP stream to the C entry point of the same name, and raises on a non-zero
+status.  All computation happens in the HIP kernels of the library.  If the
+library is not built, the first call raises -- there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmla.so")
+
+ROW_BYTES = 352
+HEAD_DIM = 576
+LATENT_DIM = 512
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "smla_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "nvfp4_pack_rows": ([_P, _P, _I32, _P, _I64, _P], ctypes.c_int),
+    "nvfp4_unpack_rows_f16": ([_P, _I64, _P, _I32, _P, _P], ctypes.c_int),
+    "sparse_mla_decode": ([_P, _P, _I64, _P, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P], ctypes.c_int),
+    "smla_choose_num_splits": ([_I32, _I32, _I32], _I32),
+    "smla_decode_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
+    "sparse_mla_combine": ([_P, _P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
+    "nvfp4_stage_fp8": ([_P, _I64, _P, _I32, _I32, _P, _P], ctypes.c_int),
+    "sparse_mla_decode_fp8rows": ([_P, _P, _P, _I64, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P], ctypes.c_int),
+}
+
+EXPORTS = tuple(_SIGS)
+
+
+class SmlaError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libsmla.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SmlaError(f"{LIB_PATH} is not built; run `python -m sparse_mla_decode_04_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = lib().smla_status_string(status).decode()
+        raise SmlaError(f"{what} failed: {msg} ({status})")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def nvfp4_pack_rows(src, slots, kv_pool):
+    """Quantize fp16 rows src[n, 576] into 352-byte rows of kv_pool[N, 352] at slots[n]."""
+    n = src.shape[0] if src.dim() == 2 else -1
+    p_src = _dev(src, "src", torch.float16, (n, HEAD_DIM))
+    p_slots = _dev(slots, "slots", torch.int32, (n,))
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_BYTES:
+        raise ValueError("kv_pool must be uint8 [N, 352]")
+    p_pool = _dev(kv_pool, "kv_pool", torch.uint8)
+    _check(lib().nvfp4_pack_rows(p_src, p_slots, n, p_pool, kv_pool.shape[0], _stream()), "nvfp4_pack_rows")
+
+
+def nvfp4_unpack_rows_f16(kv_pool, rows, out=None):
+    """fp16 [n, 576] decode of the cache rows `rows` (int32 [n])."""
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_BYTES:
+        raise ValueError("kv_pool must be uint8 [N, 352]")
+    n = rows.shape[0]
+    if out is None:
+        out = torch.empty((n, HEAD_DIM), dtype=torch.float16, device=kv_pool.device)
+    _check(lib().nvfp4_unpack_rows_f16(_dev(kv_pool, "kv_pool", torch.uint8), kv_pool.shape[0],
+                                       _dev(rows, "rows", torch.int32, (n,)), n,
+                                       _dev(out, "out", torch.float16, (n, HEAD_DIM)), _stream()),
+           "nvfp4_unpack_rows_f16")
+    return out
+
+
+def choose_num_splits(T, H, topk):
+    return int(lib().smla_choose_num_splits(T, H, topk))
+
+
+def decode_workspace_bytes(T, H, topk, num_splits=0):
+    return int(lib().smla_decode_workspace_bytes(T, H, topk, num_splits))
+
+
+def make_workspace(T, H, topk, num_splits=0, device="cuda"):
+    """Zero-filled workspace for sparse_mla_decode (uint8 tensor, possibly empty)."""
+    nb = decode_workspace_bytes(T, H, topk, num_splits)
+    return torch.zeros(max(nb, 16), dtype=torch.uint8, device=device)
+
+
+def _decode_common(entry, q, rows, pool_rows, indices, softmax_scale, out, lse, num_splits, workspace):
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be fp16 [T, H, 576]")
+    T, H, _ = q.shape
+    if indices.dim() != 2 or indices.shape[0] != T:
+        raise ValueError("indices must be int32 [T, topk]")
+    topk = indices.shape[1]
+    if out is None:
+        out = torch.empty((T, H, LATENT_DIM), dtype=torch.float16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(T, H, topk, num_splits, q.device)
+    p_ws = _dev(workspace, "workspace", torch.uint8)
+    p_q = _dev(q, "q", torch.float16)
+    p_idx = _dev(indices, "indices", torch.int32)
+    tail = (T, H, topk, float(softmax_scale), _dev(out, "out", torch.float16, (T, H, LATENT_DIM)),
+            _dev(lse, "lse", torch.float32, (T, H)), int(num_splits), p_ws, workspace.numel(), _stream())
+    if entry == "sparse_mla_decode":
+        st = lib().sparse_mla_decode(p_q, rows, pool_rows, p_idx, *tail)
+    else:
+        st = lib().sparse_mla_decode_fp8rows(p_q, rows, p_idx, pool_rows, *tail)
+    _check(st, entry)
+    return out, lse
+
+
+def sparse_mla_decode(q, kv_pool, indices, softmax_scale, out=None, lse=None, num_splits=0, workspace=None):
+    """Sparse MLA decode: returns (out fp16 [T, H, 512], lse fp32 [T, H])."""
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_BYTES:
+        raise ValueError("kv_pool must be uint8 [N, 352]")
+    return _decode_common("sparse_mla_decode", q, _dev(kv_pool, "kv_pool", torch.uint8), kv_pool.shape[0],
+                          indices, softmax_scale, out, lse, num_splits, workspace)
+
+
+def sparse_mla_combine(partial_out, partial_lse, out=None, lse=None):
+    """LSE merge of split results: partial_out fp32 [T, S, H, 512], partial_lse fp32 [T, S, H]."""
+    if partial_out.dim() != 4 or partial_out.shape[3] != LATENT_DIM:
+        raise ValueError("partial_out must be fp32 [T, S, H, 512]")
+    T, S, H, _ = partial_out.shape
+    if out is None:
+        out = torch.empty((T, H, LATENT_DIM), dtype=torch.float16, device=partial_out.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=partial_out.device)
+    _check(lib().sparse_mla_combine(_dev(partial_out, "partial_out", torch.float32),
+                                    _dev(partial_lse, "partial_lse", torch.float32, (T, S, H)), T, S, H,
+                                    _dev(out, "out", torch.float16, (T, H, LATENT_DIM)),
+                                    _dev(lse, "lse", torch.float32, (T, H)), _stream()),
+           "sparse_mla_combine")
+    return out, lse
+
+
+def nvfp4_stage_fp8(kv_pool, indices, staged=None):
+    """Staged pass 1: uint8 [T, topk, 576] E4M3 rows of the listed entries (zeros for empties)."""
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_BYTES:
+        raise ValueError("kv_pool must be uint8 [N, 352]")
+    T, topk = indices.shape
+    if staged is None:
+        staged = torch.empty((T, topk, HEAD_DIM), dtype=torch.uint8, device=kv_pool.device)
+    _check(lib().nvfp4_stage_fp8(_dev(kv_pool, "kv_pool", torch.uint8), kv_pool.shape[0],
+                                 _dev(indices, "indices", torch.int32), T, topk,
+                                 _dev(staged, "staged", torch.uint8, (T, topk, HEAD_DIM)), _stream()),
+           "nvfp4_stage_fp8")
+    return staged
+
+
+def sparse_mla_decode_fp8rows(q, staged, indices, pool_rows, softmax_scale, out=None, lse=None,
+                              num_splits=0, workspace=None):
+    """Staged pass 2: attention over the FP8 rows written by nvfp4_stage_fp8."""
+    T, topk = indices.shape
+    p_st = _dev(staged, "staged", torch.uint8, (T, topk, HEAD_DIM))
+    return _decode_common("sparse_mla_decode_fp8rows", q, p_st, int(pool_rows), indices, softmax_scale,
+                          out, lse, num_splits, workspace)
+
+
+def prepare_decode(q, kv_pool, indices, softmax_scale, out, lse, num_splits=0, workspace=None):
+    """Check the arguments of sparse_mla_decode once and return a zero-argument callable
+    that enqueues it on the current stream with the marshalled pointers (for loops that
+    launch the same shapes many times)."""
+    T, H, _ = q.shape
+    topk = indices.shape[1]
+    if workspace is None:
+        workspace = make_workspace(T, H, topk, num_splits, q.device)
+    args = (_dev(q, "q", torch.float16, (T, H, HEAD_DIM)), _dev(kv_pool, "kv_pool", torch.uint8),
+            ctypes.c_int64(kv_pool.shape[0]), _dev(indices, "indices", torch.int32, (T, topk)),
+            T, H, topk, ctypes.c_float(softmax_scale), _dev(out, "out", torch.float16, (T, H, LATENT_DIM)),
+            _dev(lse, "lse", torch.float32, (T, H)), int(num_splits), _dev(workspace, "workspace", torch.uint8),
+            ctypes.c_size_t(workspace.numel()))
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_BYTES:
+        raise ValueError("kv_pool must be uint8 [N, 352]")
+    fn = lib().sparse_mla_decode
+    keep = (q, kv_pool, indices, out, lse, workspace)   # keep the tensors alive
+
+    def call():
+        st = fn(*args, _stream())
+        if st != 0:
+            _check(st, "sparse_mla_decode")
+    call.tensors = keep
+    return call
+
+
+def prepare_pack(src, slots, kv_pool):
+    """Like prepare_decode, for nvfp4_pack_rows."""
+    n = src.shape[0]
+    args = (_dev(src, "src", torch.float16, (n, HEAD_DIM)), _dev(slots, "slots", torch.int32, (n,)), n,
+            _dev(kv_pool, "kv_pool", torch.uint8), ctypes.c_int64(kv_pool.shape[0]))
+    fn = lib().nvfp4_pack_rows
+    keep = (src, slots, kv_pool)
+
+    def call():
+        st = fn(*args, _stream())
+        if st != 0:
+            _check(st, "nvfp4_pack_rows")
+    call.tensors = keep
+    return call

@@ -1,0 +1,185 @@
+// C ABI of libsmla.so: argument checks, the batch-sized split heuristic, workspace
+// layout and kernel launches.  Declarations and contracts: include/smla.h.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "smla.h"
+#include "smla_decode.hpp"
+#include "smla_launch.hpp"
+
+namespace {
+
+using namespace smla;
+
+constexpr int kWgPerCu = 2;           // decode workgroups resident per CU (LDS / VGPR budget)
+constexpr int kMinChunksPerWg = 2;    // below this the partial results outweigh the rows
+constexpr int kMaxTopk = 65536;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+int32_t auto_splits(int32_t T, int32_t H, int32_t topk) {
+  const int64_t cpt = (topk + kChunkRows - 1) / kChunkRows;
+  const int64_t C = (int64_t)T * cpt;
+  const int HG = H / kHeadGroup;
+  int64_t G = (int64_t)cu_count() * kWgPerCu / (HG > 0 ? HG : 1);
+  const int64_t cap = C / kMinChunksPerWg;
+  if (G > cap) G = cap;
+  if (G < 1) G = 1;
+  if (G > C) G = C;
+  return (int32_t)G;
+}
+
+bool decode_shape_ok(int32_t T, int32_t H, int32_t topk) {
+  return T >= 0 && H > 0 && topk >= 1 && topk <= kMaxTopk;
+}
+
+int check_decode(const void* q, const void* rows, int64_t pool_rows, const int32_t* idx, int32_t T,
+                 int32_t H, int32_t topk, float softmax_scale, const void* out, const float* lse,
+                 int32_t num_splits) {
+  if (!decode_shape_ok(T, H, topk) || num_splits < 0 || pool_rows < 0 || !isfinite(softmax_scale))
+    return SMLA_ERR_INVALID_ARG;
+  if (H % kHeadGroup != 0) return SMLA_ERR_UNSUPPORTED;
+  if (T == 0) return SMLA_OK;
+  if (!q || !rows || !idx || !out || !lse) return SMLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(rows) || !aligned4(idx) || !aligned16(out) || !aligned4(lse))
+    return SMLA_ERR_INVALID_ARG;
+  return SMLA_OK;
+}
+
+int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
+               const int32_t* idx, int32_t T, int32_t H, int32_t topk, float softmax_scale,
+               void* out, float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_decode(q, rows, pool_rows, idx, T, H, topk, softmax_scale, out, lse, num_splits);
+  if (st != SMLA_OK || T == 0) return st;
+  const int32_t G = num_splits > 0 ? num_splits : auto_splits(T, H, topk);
+  const DecodePlan p = make_plan(T, H, topk, G);
+  if (p.bytes > 0 && (ws == nullptr || ws_bytes < p.bytes || !aligned16(ws))) return SMLA_ERR_WORKSPACE;
+  DecodeArgs a;
+  a.q = q;
+  a.rows = rows;
+  a.pool_rows = pool_rows;
+  a.idx = idx;
+  a.T = T;
+  a.H = H;
+  a.topk = topk;
+  a.cpt = p.cpt;
+  a.chunks = p.chunks;
+  a.G = p.G;
+  a.max_seg = p.max_seg;
+  a.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = (float*)((char*)ws + p.part_o_off);
+  a.part_lse = (float*)((char*)ws + p.part_lse_off);
+  a.counters = (int32_t*)((char*)ws + p.counters_off);
+  const hipError_t e = fp8rows ? launch_decode_fp8rows(a, (hipStream_t)stream)
+                               : launch_decode_nvfp4(a, (hipStream_t)stream);
+  return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+SMLA_API const char* smla_status_string(int status) {
+  switch (status) {
+    case SMLA_OK: return "SMLA_OK";
+    case SMLA_ERR_INVALID_ARG: return "SMLA_ERR_INVALID_ARG";
+    case SMLA_ERR_UNSUPPORTED: return "SMLA_ERR_UNSUPPORTED";
+    case SMLA_ERR_WORKSPACE: return "SMLA_ERR_WORKSPACE";
+    case SMLA_ERR_LAUNCH: return "SMLA_ERR_LAUNCH";
+    default: return "SMLA_ERR_UNKNOWN";
+  }
+}
+
+SMLA_API int nvfp4_pack_rows(const void* src, const int32_t* slots, int32_t n, void* pool, int64_t pool_rows,
+                    void* stream) {
+  if (n < 0 || pool_rows < 0) return SMLA_ERR_INVALID_ARG;
+  if (n == 0) return SMLA_OK;
+  if (!src || !slots || !pool || !aligned16(src) || !aligned4(slots) || !aligned16(pool))
+    return SMLA_ERR_INVALID_ARG;
+  return launch_pack(src, slots, n, pool, pool_rows, (hipStream_t)stream) == hipSuccess ? SMLA_OK
+                                                                                        : SMLA_ERR_LAUNCH;
+}
+
+SMLA_API int nvfp4_unpack_rows_f16(const void* pool, int64_t pool_rows, const int32_t* rows, int32_t n,
+                          void* out, void* stream) {
+  if (n < 0 || pool_rows < 0) return SMLA_ERR_INVALID_ARG;
+  if (n == 0) return SMLA_OK;
+  if (!pool || !rows || !out || !aligned16(pool) || !aligned4(rows) || !aligned16(out))
+    return SMLA_ERR_INVALID_ARG;
+  return launch_unpack(pool, pool_rows, rows, n, out, (hipStream_t)stream) == hipSuccess
+             ? SMLA_OK
+             : SMLA_ERR_LAUNCH;
+}
+
+SMLA_API int32_t smla_choose_num_splits(int32_t T, int32_t H, int32_t topk) {
+  if (!decode_shape_ok(T, H, topk) || H % kHeadGroup != 0 || T == 0) return 0;
+  return auto_splits(T, H, topk);
+}
+
+SMLA_API size_t smla_decode_workspace_bytes(int32_t T, int32_t H, int32_t topk, int32_t num_splits) {
+  if (!decode_shape_ok(T, H, topk) || H % kHeadGroup != 0 || T == 0 || num_splits < 0) return 0;
+  const int32_t G = num_splits > 0 ? num_splits : auto_splits(T, H, topk);
+  return make_plan(T, H, topk, G).bytes;
+}
+
+SMLA_API int sparse_mla_decode(const void* q, const void* pool, int64_t pool_rows, const int32_t* idx,
+                      int32_t T, int32_t H, int32_t topk, float softmax_scale, void* out,
+                      float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
+  return run_decode(false, q, pool, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
+                    num_splits, ws, ws_bytes, stream);
+}
+
+SMLA_API int sparse_mla_combine(const float* part_o, const float* part_lse, int32_t T, int32_t S, int32_t H,
+                       void* out, float* lse, void* stream) {
+  if (T < 0 || S < 1 || H <= 0) return SMLA_ERR_INVALID_ARG;
+  if (H % kHeadGroup != 0) return SMLA_ERR_UNSUPPORTED;
+  if (T == 0) return SMLA_OK;
+  if (!part_o || !part_lse || !out || !lse || !aligned16(part_o) || !aligned4(part_lse) ||
+      !aligned16(out) || !aligned4(lse))
+    return SMLA_ERR_INVALID_ARG;
+  return launch_combine(part_o, part_lse, T, S, H, out, lse, (hipStream_t)stream) == hipSuccess
+             ? SMLA_OK
+             : SMLA_ERR_LAUNCH;
+}
+
+SMLA_API int nvfp4_stage_fp8(const void* pool, int64_t pool_rows, const int32_t* idx, int32_t T, int32_t topk,
+                    void* staged, void* stream) {
+  if (T < 0 || topk < 1 || topk > kMaxTopk || pool_rows < 0) return SMLA_ERR_INVALID_ARG;
+  if (T == 0) return SMLA_OK;
+  if (!pool || !idx || !staged || !aligned16(pool) || !aligned4(idx) || !aligned16(staged))
+    return SMLA_ERR_INVALID_ARG;
+  return launch_stage_fp8(pool, pool_rows, idx, (int64_t)T * topk, staged, (hipStream_t)stream) ==
+                 hipSuccess
+             ? SMLA_OK
+             : SMLA_ERR_LAUNCH;
+}
+
+SMLA_API int sparse_mla_decode_fp8rows(const void* q, const void* staged, const int32_t* idx,
+                              int64_t pool_rows, int32_t T, int32_t H, int32_t topk,
+                              float softmax_scale, void* out, float* lse, int32_t num_splits,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return run_decode(true, q, staged, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
+                    num_splits, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,22 @@
+// Host-side launch entry points of the kernels (internal to libsmla.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "smla_decode.hpp"
+
+namespace smla {
+
+hipError_t launch_pack(const void* src, const int32_t* slots, int32_t n, void* pool,
+                       int64_t pool_rows, hipStream_t s);
+hipError_t launch_unpack(const void* pool, int64_t pool_rows, const int32_t* rows, int32_t n,
+                         void* out, hipStream_t s);
+hipError_t launch_stage_fp8(const void* pool, int64_t pool_rows, const int32_t* idx,
+                            int64_t entries, void* staged, hipStream_t s);
+hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_fp8rows(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t T, int32_t S,
+                          int32_t H, void* out, float* lse, hipStream_t s);
+
+}  // namespace smla

@@ -1,0 +1,73 @@
+"""Shared glue for the GPU parity tests and the benchmark's checks: building a
+device pool through the library's own row writer, the oracle's view of the same
+pool (quantized from the same fp16 source rows by the oracle), and the parity
+tolerances."""
+
+import numpy as np
+
+from sparse_mla_decode_04_amd import workloads as W
+
+# Attention tolerance: max |out - ref| <= OUT_RTOL * max |ref| over a launch's checked
+# outputs; |lse - ref| <= LSE_ATOL on finite entries, and -inf exactly where ref is -inf.
+OUT_RTOL = 2e-3
+LSE_ATOL = 1e-3
+
+
+def pool_source_all(wl):
+    """fp16 [N, 576] source rows of the whole pool, with the workload's new rows written
+    at their slots (the cache write that precedes decode)."""
+    src = np.concatenate([c for _, c in W.pool_source_chunks(wl)], axis=0)
+    new, slots = W.new_rows(wl)
+    if len(slots):
+        src[slots] = new
+    return src
+
+
+class OracleRows:
+    """Pool rows as the oracle sees them: quantized by the oracle's own row writer from
+    the fp16 source rows, built on demand for the requested row ids."""
+
+    def __init__(self, src):
+        self.src = src
+
+    def __getitem__(self, ids):
+        import oracle
+        ids = np.asarray(ids, dtype=np.int64)
+        return oracle.nvfp4_pack_rows_ref(self.src[ids])
+
+
+def build_device_pool(src, device, chunk=65536):
+    """Pack the fp16 source rows into a device pool with nvfp4_pack_rows."""
+    import torch
+    import sparse_mla_decode_04_amd as smla
+    N = src.shape[0]
+    pool = torch.zeros((N, 352), dtype=torch.uint8, device=device)
+    for a in range(0, N, chunk):
+        b = min(N, a + chunk)
+        s = torch.from_numpy(np.ascontiguousarray(src[a:b])).to(device)
+        slots = torch.arange(a, b, dtype=torch.int32, device=device)
+        smla.nvfp4_pack_rows(s, slots, pool)
+    return pool
+
+
+def parity_errors(out, lse, ref_out, ref_lse):
+    """(max abs out error / max |ref|, max abs lse error on finite, -inf pattern equal)."""
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref_out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    rl = np.asarray(ref_lse, dtype=np.float64)
+    scale = max(np.max(np.abs(ref)), 1e-30)
+    out_err = float(np.max(np.abs(out - ref))) / scale if out.size else 0.0
+    fin = np.isfinite(rl)
+    lse_err = float(np.max(np.abs(lse[fin] - rl[fin]))) if np.any(fin) else 0.0
+    inf_ok = bool(np.array_equal(np.isneginf(lse), np.isneginf(rl)) and not np.any(np.isnan(lse)))
+    return out_err, lse_err, inf_ok
+
+
+def assert_parity(out, lse, ref_out, ref_lse, what=""):
+    oe, le, ok = parity_errors(out, lse, ref_out, ref_lse)
+    assert np.all(np.isfinite(np.asarray(out, dtype=np.float64))), f"{what}: non-finite output"
+    assert ok, f"{what}: -inf pattern of lse differs"
+    assert oe <= OUT_RTOL, f"{what}: out error {oe:.3e} > {OUT_RTOL} * max|ref|"
+    assert le <= LSE_ATOL, f"{what}: lse error {le:.3e} > {LSE_ATOL}"
+    return oe, le

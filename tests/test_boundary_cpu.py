@@ -1,0 +1,90 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/smla.h declares, and rejects bad arguments on the host (before any
+launch) with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mla_decode_04_amd as smla
+from sparse_mla_decode_04_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "smla.h")).read()
+    return set(re.findall(r"SMLA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libsmla.so not built")
+    return smla.lib()
+
+
+def test_header_and_binding_agree():
+    assert _declared() == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    assert L.smla_status_string(0) == b"SMLA_OK"
+    assert L.smla_status_string(-3) == b"SMLA_ERR_WORKSPACE"
+    assert L.smla_status_string(-99) == b"SMLA_ERR_UNKNOWN"
+
+
+def test_workspace_and_split_queries(L):
+    assert smla.choose_num_splits(35, 16, 2048) >= 1
+    assert smla.decode_workspace_bytes(35, 16, 2048, 0) > 0
+    assert smla.decode_workspace_bytes(35, 24, 2048, 0) == 0      # unsupported H
+    assert smla.decode_workspace_bytes(0, 16, 2048, 0) == 0
+    # one workgroup per head group owning every token: no partials needed beyond one slot
+    assert smla.decode_workspace_bytes(4, 16, 2048, 1) < smla.decode_workspace_bytes(4, 16, 2048, 32)
+
+
+P = ctypes.c_void_p
+
+
+def _decode(L, q=16, pool=16, idx=16, T=1, H=16, topk=64, scale=0.1, out=16, lse=16, ns=0, ws=None, wsb=1 << 30):
+    return L.sparse_mla_decode(P(q), P(pool), 100, P(idx), T, H, topk, scale, P(out), P(lse), ns,
+                               P(ws), wsb, None)
+
+
+def test_decode_argument_checks(L):
+    assert _decode(L, q=None) == -1
+    assert _decode(L, q=8) == -1                   # misaligned
+    assert _decode(L, H=24) == -2                  # not a multiple of 16
+    assert _decode(L, topk=0) == -1
+    assert _decode(L, topk=70000) == -1
+    assert _decode(L, ns=-1) == -1
+    assert _decode(L, scale=float("nan")) == -1
+    assert _decode(L, ws=None) == -3               # workspace missing
+    assert _decode(L, ws=16, wsb=10) == -3         # workspace too small
+    assert _decode(L, T=0, q=None, pool=None, idx=None, out=None, lse=None) == 0   # nothing to do
+
+
+def test_other_entry_points_check_arguments(L):
+    assert L.nvfp4_pack_rows(None, None, 0, None, 10, None) == 0        # n == 0: no-op
+    assert L.nvfp4_pack_rows(None, P(16), 3, P(16), 10, None) == -1
+    assert L.nvfp4_pack_rows(P(16), P(16), -1, P(16), 10, None) == -1
+    assert L.nvfp4_unpack_rows_f16(P(16), 10, None, 2, P(16), None) == -1
+    assert L.sparse_mla_combine(P(16), P(16), 2, 0, 16, P(16), P(16), None) == -1
+    assert L.sparse_mla_combine(P(16), P(16), 2, 2, 8, P(16), P(16), None) == -2
+    assert L.nvfp4_stage_fp8(P(16), 10, P(16), 2, 0, P(16), None) == -1
+    assert L.sparse_mla_decode_fp8rows(P(16), P(16), P(16), 10, 1, 16, 64, 0.1, P(16), P(16), 0,
+                                       None, 0, None) == -3
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises((ValueError, TypeError)):
+        smla.nvfp4_pack_rows(torch.zeros(2, 576, dtype=torch.float16), torch.zeros(2, dtype=torch.int32),
+                             torch.zeros(4, 352, dtype=torch.uint8))
