@@ -187,12 +187,15 @@ __global__ __launch_bounds__(256, kFp8 ? 1 : 2) void sparse_mla_decode_kernel(De
   SMLA_LDS uint8_t* ring1 = (SMLA_LDS uint8_t*)sm.ring[1];
 
   // ---- prologue: chunks 0 and 1 in flight, chunk 0 in LDS
+  // Index lists run two chunks ahead of the row loads: loads complete in issue order, so
+  // waiting for an index load also waits for every load issued before it.
   Stage<kFp8> s0, s1;
-  int32_t idx_next = load_idx(A, c_lo, wid, lane);
-  issue(A, c_lo, idx_next, s0, wid, lane);
-  idx_next = (n > 1) ? load_idx(A, c_lo + 1, wid, lane) : -1;
-  if (n > 1) issue(A, c_lo + 1, idx_next, s1, wid, lane);
-  idx_next = (n > 2) ? load_idx(A, c_lo + 2, wid, lane) : -1;
+  const int32_t idx0 = load_idx(A, c_lo, wid, lane);
+  const int32_t idx1 = (n > 1) ? load_idx(A, c_lo + 1, wid, lane) : -1;
+  int32_t idx_a = (n > 2) ? load_idx(A, c_lo + 2, wid, lane) : -1;   // chunk i+2 at step i
+  int32_t idx_b = (n > 3) ? load_idx(A, c_lo + 3, wid, lane) : -1;   // chunk i+3 at step i
+  issue(A, c_lo, idx0, s0, wid, lane);
+  if (n > 1) issue(A, c_lo + 1, idx1, s1, wid, lane);
   QStage qst;
   issue_q(A, c_lo / cpt, hg, qst);
   uint64_t vm_cur = valid_mask(A, s0, lane);
@@ -222,10 +225,11 @@ __global__ __launch_bounds__(256, kFp8 ? 1 : 2) void sparse_mla_decode_kernel(De
     // the next chunk starts a new token: fetch its query tile, committed after this chunk
     const bool next_new_tok = (i + 1 < n) && (cin == cpt - 1);
     if (next_new_tok) issue_q(A, t + 1, hg, qst);
-    // prefetch chunk i+2 into the free register set, index list of chunk i+3
+    // prefetch chunk i+2 into the free register set, index list of chunk i+4
     if (i + 2 < n) {
-      issue(A, c + 2, idx_next, freeS, wid, lane);
-      idx_next = (i + 3 < n) ? load_idx(A, c + 3, wid, lane) : -1;
+      issue(A, c + 2, idx_a, freeS, wid, lane);
+      idx_a = idx_b;
+      idx_b = (i + 4 < n) ? load_idx(A, c + 4, wid, lane) : -1;
     }
 
     // ---- QK^T for rows 16*wid + r16 (A operand), 16 heads (B operand)
@@ -365,11 +369,11 @@ __global__ __launch_bounds__(256, kFp8 ? 1 : 2) void sparse_mla_decode_kernel(De
         const int64_t slot = ((int64_t)hg * G + w) * A.max_seg + (t - c_lo / cpt);
         float* po = A.part_o + (slot * kHeadGroup + r16) * kLatent;
 #pragma unroll
-        for (int k = 0; k < 8; k++) *(f32x4*)(po + 16 * (8 * wid + k) + 4 * g) = O[k] * inv;
-        if (wid == 0 && lane < kHeadGroup) A.part_lse[slot * kHeadGroup + r16] = lse_nat;
-        // publish, count, and let the last workgroup of this token merge
+        for (int k = 0; k < 8; k++) store_coherent(po + 16 * (8 * wid + k) + 4 * g, O[k] * inv);
+        if (wid == 0 && lane < kHeadGroup) store_coherent(A.part_lse + slot * kHeadGroup + r16, lse_nat);
+        // publish (stores complete), count, and let the last workgroup of this token merge
         const int64_t w_lo = wg_of_chunk(tok0, C, G), w_hi = wg_of_chunk(tok0 + cpt - 1, C, G);
-        __threadfence();
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
           int32_t* cnt = A.counters + (int64_t)hg * A.T + t;
@@ -396,7 +400,6 @@ __global__ __launch_bounds__(256, kFp8 ? 1 : 2) void sparse_mla_decode_kernel(De
   for (int k = 0; k < 2; k++) {
     const int64_t t = k == 0 ? pend0 : pend1;
     if (t < 0) continue;
-    __threadfence();
     const int64_t tok0 = t * cpt;
     const int64_t w_lo = wg_of_chunk(tok0, C, G), w_hi = wg_of_chunk(tok0 + cpt - 1, C, G);
     auto part = [&](int s, const float** o, const float** l) {
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(256, kFp8 ? 1 : 2) void sparse_mla_decode_kernel(De
       *o = A.part_o + sl * kHeadGroup * kLatent;
       *l = A.part_lse + sl * kHeadGroup;
     };
-    lse_merge16((int)(w_hi - w_lo + 1), part,
+    lse_merge16<true>((int)(w_hi - w_lo + 1), part,
                 (f16*)A.out + ((int64_t)t * A.H + kHeadGroup * hg) * kLatent, kLatent,
                 A.lse + (int64_t)t * A.H + kHeadGroup * hg);
   }
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(256) void sparse_mla_combine_kernel(const float* __
     *o = part_o + base * kLatent;
     *l = part_lse + base;
   };
-  lse_merge16(S, part, out + ((int64_t)t * H + kHeadGroup * hg) * kLatent, kLatent,
+  lse_merge16<false>(S, part, out + ((int64_t)t * H + kHeadGroup * hg) * kLatent, kLatent,
               lse + (int64_t)t * H + kHeadGroup * hg);
 }
 
