@@ -13,9 +13,9 @@ namespace {
 
 using namespace smla;
 
-constexpr int kWgPerCu = 2;           // decode workgroups resident per CU (LDS / VGPR budget)
-constexpr int kMinChunksPerWg = 2;    // below this the partial results outweigh the rows
+constexpr int kMinTilesPerWg = 2;     // below this the partial results outweigh the rows
 constexpr int kMaxTopk = 65536;
+constexpr uint64_t kMaxBufferBytes = 0xFFFFFFE0ull;   // byte range of one buffer resource
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -35,12 +35,13 @@ int cu_count() {
   return cus;
 }
 
-int32_t auto_splits(int32_t T, int32_t H, int32_t topk) {
-  const int64_t cpt = (topk + kChunkRows - 1) / kChunkRows;
+int32_t auto_splits(bool fp8rows, int32_t T, int32_t H, int32_t topk) {
+  const int64_t cpt = (topk + kTileRows - 1) / kTileRows;
   const int64_t C = (int64_t)T * cpt;
-  const int HG = H / kHeadGroup;
-  int64_t G = (int64_t)cu_count() * kWgPerCu / (HG > 0 ? HG : 1);
-  const int64_t cap = C / kMinChunksPerWg;
+  const int NG = heads_per_block_groups(H, topk);
+  const int HB = H / (kHeadGroup * NG);
+  int64_t G = (int64_t)cu_count() * decode_wgs_per_cu(fp8rows, NG) / (HB > 0 ? HB : 1);
+  const int64_t cap = C / kMinTilesPerWg;
   if (G > cap) G = cap;
   if (G < 1) G = 1;
   if (G > C) G = C;
@@ -69,8 +70,15 @@ int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
                void* out, float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
   int st = check_decode(q, rows, pool_rows, idx, T, H, topk, softmax_scale, out, lse, num_splits);
   if (st != SMLA_OK || T == 0) return st;
-  const int32_t G = num_splits > 0 ? num_splits : auto_splits(T, H, topk);
+  // every buffer the kernels address through a buffer resource must fit its byte range
+  const uint64_t idx_bytes = (uint64_t)T * topk * 4;
+  const uint64_t q_bytes = (uint64_t)T * H * 576 * 2;
+  const uint64_t rows_bytes = fp8rows ? (uint64_t)T * topk * 576 : (uint64_t)pool_rows * 352;
+  if (idx_bytes > kMaxBufferBytes || rows_bytes > kMaxBufferBytes || q_bytes > kMaxBufferBytes)
+    return SMLA_ERR_UNSUPPORTED;
+  const int32_t G = num_splits > 0 ? num_splits : auto_splits(fp8rows, T, H, topk);
   const DecodePlan p = make_plan(T, H, topk, G);
+  if (p.bytes > kMaxBufferBytes) return SMLA_ERR_UNSUPPORTED;
   if (p.bytes > 0 && (ws == nullptr || ws_bytes < p.bytes || !aligned16(ws))) return SMLA_ERR_WORKSPACE;
   DecodeArgs a;
   a.q = q;
@@ -81,15 +89,20 @@ int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
   a.H = H;
   a.topk = topk;
   a.cpt = p.cpt;
-  a.chunks = p.chunks;
+  a.tiles = p.tiles;
   a.G = p.G;
-  a.max_seg = p.max_seg;
+  a.HB = p.HB;
+  a.rows_bytes = (uint32_t)rows_bytes;
+  a.idx_bytes = (uint32_t)idx_bytes;
+  a.q_bytes = (uint32_t)q_bytes;
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
   a.out = out;
   a.lse = lse;
   a.part_o = (float*)((char*)ws + p.part_o_off);
   a.part_lse = (float*)((char*)ws + p.part_lse_off);
   a.counters = (int32_t*)((char*)ws + p.counters_off);
+  a.part_o_bytes = (uint32_t)(p.part_lse_off - p.part_o_off);
+  a.part_lse_bytes = (uint32_t)(p.counters_off - p.part_lse_off);
   const hipError_t e = fp8rows ? launch_decode_fp8rows(a, (hipStream_t)stream)
                                : launch_decode_nvfp4(a, (hipStream_t)stream);
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
@@ -133,12 +146,12 @@ SMLA_API int nvfp4_unpack_rows_f16(const void* pool, int64_t pool_rows, const in
 
 SMLA_API int32_t smla_choose_num_splits(int32_t T, int32_t H, int32_t topk) {
   if (!decode_shape_ok(T, H, topk) || H % kHeadGroup != 0 || T == 0) return 0;
-  return auto_splits(T, H, topk);
+  return auto_splits(false, T, H, topk);
 }
 
 SMLA_API size_t smla_decode_workspace_bytes(int32_t T, int32_t H, int32_t topk, int32_t num_splits) {
   if (!decode_shape_ok(T, H, topk) || H % kHeadGroup != 0 || T == 0 || num_splits < 0) return 0;
-  const int32_t G = num_splits > 0 ? num_splits : auto_splits(T, H, topk);
+  const int32_t G = num_splits > 0 ? num_splits : auto_splits(false, T, H, topk);
   return make_plan(T, H, topk, G).bytes;
 }
 
@@ -157,6 +170,7 @@ SMLA_API int sparse_mla_combine(const float* part_o, const float* part_lse, int3
   if (!part_o || !part_lse || !out || !lse || !aligned16(part_o) || !aligned4(part_lse) ||
       !aligned16(out) || !aligned4(lse))
     return SMLA_ERR_INVALID_ARG;
+  if ((uint64_t)T * S * H * 512 * 4 > kMaxBufferBytes) return SMLA_ERR_UNSUPPORTED;
   return launch_combine(part_o, part_lse, T, S, H, out, lse, (hipStream_t)stream) == hipSuccess
              ? SMLA_OK
              : SMLA_ERR_LAUNCH;

@@ -3,130 +3,156 @@
 // "Prime Intellect Launches Prime Inference, Serving 600B Tokens Daily", section
 // "Four-bit caches make room": for every decode token the kernel loads only the cache
 // rows named by the sparse indexer's 2,048-entry list, unpacks the NVFP4 values on chip
-// (no FP8 staging buffer in HBM), and runs attention with FP16 operands and FP32
+// (no FP8 staging buffer in HBM) and runs attention with FP16 operands and FP32
 // accumulation; empty list entries cost no load.  The page's kernel overlaps unpacking
-// with scoring/accumulation through a three-slot pipeline over warp groups and sizes
-// SM clusters by the token batch; the gfx950 design below keeps the overlap and the
-// batch-sized decomposition but maps them onto wave64 / MFMA / LDS:
+// with scoring and accumulation through a three-slot pipeline over warp groups and sizes
+// SM clusters by the token batch.  The gfx950 design keeps the overlap and the
+// batch-sized decomposition, mapped onto wave64, LDS DMA and MFMA:
 //
-//  * Workgroup = 4 waves, one 16-head group, a contiguous range of 64-row chunks of the
-//    flattened (token, chunk) sequence (stream-K split, see smla_decode.hpp).  Block ids
-//    are remapped so that consecutive ranges -- which share tokens -- run on one XCD.
-//  * Gather: each wave fetches its 16 rows of a chunk with coalesced 16-byte loads
-//    (22 per 352-byte row) into registers two chunks ahead, and stores them into a
-//    double-buffered LDS slot one chunk ahead.  Empty entries issue no load and store
-//    zeros.  Several waves per SIMD keep MFMA, VALU unpack and loads in flight at once.
-//  * QK^T: wave w scores rows 16w..16w+15 of the chunk against the 16 heads with
-//    v_mfma_f32_16x16x32_f16 (M = rows, N = heads, K = 576 in 18 steps).  Each lane
-//    unpacks its own row's codes straight into the A operand (E2M1 -> fp16 by the
-//    hardware convert, times the E4M3 group scale by an exact fp16 multiply); the query
-//    tile stays in registers as the B operand.
-//  * Online softmax in fp32 (base-2, scores pre-scaled by softmax_scale*log2 e), with a
-//    shared running maximum that is only raised when a chunk's maximum exceeds it by
-//    more than 8 (so rescaling of the accumulator is rare and probabilities stay <= 256
-//    in fp16).  Empty entries get probability 0.
+//  * Workgroup = 4 waves, one block of 16*NG heads, one stream-K range of 64-row tiles
+//    (smla_decode.hpp).  Block ids are remapped so that the head blocks of a range, and
+//    neighbouring ranges, run on one XCD (shared L2).  With 16 heads a workgroup fits in
+//    half of a CU's LDS, so two of them share each CU and hide each other's waits.
+//  * Gather: the rows of tile i+D are fetched while tile i is computed, straight from HBM
+//    into a ring of D+1 LDS slots with buffer_load ... lds (16 bytes per lane, no register
+//    staging).  Wave w fetches rows 16w..16w+15 of a tile; its part of a slot is stored
+//    piece-major ([16-byte piece][row]) so that the row reads of the scoring step are
+//    free of bank conflicts.  Empty entries use an out-of-range buffer offset: the
+//    hardware returns zeros and touches no memory.  The index list runs two tiles ahead
+//    of the rows through the same DMA path, so every wait is an exact count of in-order
+//    vector memory operations.
+//  * QK^T: wave w scores its own 16 rows against the block's heads with
+//    v_mfma_f32_16x16x32_f16 (M = rows, N = heads, K = 576 in 18 steps, in two
+//    independent accumulation chains).  Each lane unpacks its row's codes straight into
+//    the A operand (hardware E2M1 -> fp16 convert, times the E4M3 group scale by an exact
+//    fp16 multiply) once for all NG head groups; the query stays in registers as the B
+//    operand.
+//  * Online softmax in fp32, base 2 (scores pre-scaled by softmax_scale*log2 e), with a
+//    per-head reference maximum shared by the four waves.  A wave keeps the reference
+//    unless its own rows exceed it by more than 8, in which case it uses its own maximum;
+//    probabilities therefore stay <= 256 in fp16.  After the tile's barrier the new
+//    reference is the largest one any wave used, and the few probabilities computed
+//    against a smaller one are scaled down (rare: the reference settles after the first
+//    tiles).  Empty entries get probability 0.
 //  * PV: wave w owns output features 128w..128w+127 (8 tiles of 16 = one scale group
-//    each) for all 16 heads and all 64 rows: O^T += V^T P^T with M = features, N = heads,
-//    K = rows.  The V^T operand comes straight from the raw nibbles through the LDS
-//    4-bit transpose read (ds_read_b64_tr_b4: 16 rows of one feature per lane), scaled
-//    by a per-chunk fp16 table of the rows' E4M3 scales (zero for empty rows); P^T is
-//    exchanged through LDS.
-//  * Epilogue: a workgroup that owns a whole token writes out = O/l and lse directly;
-//    otherwise it writes its normalized partial and LSE, and the last workgroup of the
-//    token (device-scope counter) merges the partials (smla_combine.hpp).
+//    each) for all heads of the block over the tile's 64 rows: O^T += V^T P^T with
+//    M = features, N = heads, K = rows.  V^T comes straight from the raw nibbles through
+//    the LDS 4-bit transpose read (ds_read_b64_tr_b4: 16 rows of one feature per lane),
+//    scaled by a per-tile fp16 table of the rows' E4M3 group scales.
+//  * Epilogue: a range that covers a whole token writes out = O/l and lse directly;
+//    otherwise it writes its normalized partial and LSE (device-coherent stores), and
+//    after its last tile counts itself in; the last range of a token merges the partials
+//    (smla_combine.hpp).
 //
-// The same skeleton, instantiated with kFp8 = true, is pass 2 of the staged variant: it
-// attends over 576-byte FP8 E4M3 rows written to HBM by pass 1 (one per list entry),
-// reading V^T through the 8-bit LDS transpose read instead of the 4-bit one.
+// One barrier per tile between each wave's QK (which fills the probability and scale
+// tables and waits for its own DMA) and everyone's PV (which reads every wave's rows).  The ring slot
+// refilled after the barrier of tile i was last read by the PV of tile i-1, which every
+// wave has finished by then.  With a distance of one tile (two slots) a second barrier at
+// the start of each tile frees the other slot, so the next tile's rows are requested a
+// whole tile of work ahead.
+//
+// The query of the first token of a range is loaded into registers directly; the query of
+// every later token is staged into LDS by the same DMA path, issued just before the rows of
+// the token's first tile, and moved to registers at that tile.
+//
+// The same skeleton with kFp8 = true is pass 2 of the staged variant: it attends over
+// 576-byte FP8 E4M3 rows written to HBM by pass 1 (one per list entry), reading V^T
+// through the 8-bit LDS transpose read.
 #include "smla_combine.hpp"
 #include "smla_device.hpp"
 #include "smla_launch.hpp"
+
+// The LDS DMA sequences below set m0 themselves and declare it clobbered.
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace smla {
 
 namespace {
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = 4;
-constexpr int kWaveRows = 16;                               // rows gathered/scored per wave
-constexpr int kPad = 72;                                   // fp16 row stride of sc/pb tables
-constexpr float kRescaleSlack = 8.0f;                      // log2 units
-constexpr int kQStride = kHeadDim + 8;                     // fp16 stride of the LDS query tile
-constexpr int kQPieces = kHeadGroup * kHeadDim * 2 / 16;   // 1152 16-byte pieces per tile
-constexpr int kQLoads = (kQPieces + 255) / 256;            // 5 per thread
+constexpr int kWR = 16;                 // rows per wave per tile
+constexpr int kPH = 72;                 // fp16 stride of the [.][tile row] tables
+constexpr float kSlack = 8.0f;          // log2 units
+constexpr uint32_t kOOB = 0xFFFFFFE0u;  // buffer offset beyond every range: reads as zero
 
 template <bool kFp8>
-struct Fmt {
-  static constexpr int kRB = kFp8 ? kHeadDim : kRowBytes;          // bytes per row
-  static constexpr int kPiecesPerRow = kRB / 16;                   // 22 or 36
-  static constexpr int kWavePieces = kWaveRows * kPiecesPerRow;    // 352 or 576
-  static constexpr int kLoads = (kWavePieces + 63) / 64;           // 6 or 9 per lane
-  static constexpr int kSlotBytes = kChunkRows * kRB;
+struct RowFmt {
+  static constexpr int kRB = kFp8 ? kHeadDim : kRowBytes;   // bytes per row in HBM
+  static constexpr int kPieces = kRB / 16;                   // 36 or 22
+  static constexpr int kLoads = (kPieces + 3) / 4;           // DMA per wave per tile: 9 or 6
+  static constexpr int kPortion = kPieces * 256;             // LDS bytes of one wave's rows
+  static constexpr int kSlot = kWaves * kPortion;            // LDS bytes of one tile
 };
 
-template <bool kFp8>
+// Query staging: the 16*NG query rows of a token (1152 bytes each) as 16-byte pieces with
+// one spare piece per row (row stride 1168 bytes keeps the register loads conflict-free),
+// filled by kLoads DMA instructions of 1 KB.
+template <int NG>
+struct QFmt {
+  static constexpr int kSlots = kHeadGroup * NG * 73;        // 72 pieces + 1 spare per head
+  static constexpr int kLoads = (kSlots + 63) / 64;          // 19 or 37
+  static constexpr int kBytes = kLoads * 1024;
+};
+
+// Staging buffers for the query: one suffices unless the distance is two tiles and a
+// token may span a single tile (then the query of the token after next would overwrite
+// the one being read).
+template <int NG, int ST>
+constexpr int kQBufs = (ST == 3 && NG == 1) ? 2 : 1;
+
+template <int NG, int ST, bool kFp8>
 struct __attribute__((aligned(16))) Smem {
-  uint8_t ring[2][Fmt<kFp8>::kSlotBytes];   // raw rows of the chunk being scored / the next
-  f16 sc[kFp8 ? 1 : 32][kPad];              // [scale group][row] fp16 scales, 0 for empty rows
-  f16 pb[kHeadGroup][kPad];                 // [head][row] fp16 probabilities
-  f16 qs[kHeadGroup][kQStride];             // query tile of the current token, [head][576]
-  float xmax[kWaves][kHeadGroup];           // per-wave chunk maxima
-  float lsum[kWaves][kHeadGroup];           // per-wave softmax denominators
+  uint8_t ring[ST][RowFmt<kFp8>::kSlot];    // [slot][wave][piece][row] 16-byte pieces
+  uint8_t qst[kQBufs<NG, ST>][QFmt<NG>::kBytes];   // query staging [token parity]
+  int32_t idx[2][kWaves][kWR];              // index-list DMA landing zone [tile parity][wave]
+  f16 sc[2][kFp8 ? 1 : 32][kPH];            // PV scales [parity][group][tile row]
+  f16 pb[2][kHeadGroup * NG][kPH];          // probabilities [parity][head][tile row]
+  float wref[2][kWaves][kHeadGroup * NG];   // reference each wave used [parity][wave][head]
+  int wflag[2][kWaves];                     // bit 0: wave raised a reference; bit 1: wave has a row
   int flag;
 };
 
-template <bool kFp8>
-struct Stage {
-  u32x4 v[Fmt<kFp8>::kLoads];
-  int32_t idx;   // lane < 16: pool row of wave row `lane` (or -1)
-};
-
-__device__ __forceinline__ int32_t load_idx(const DecodeArgs& A, int64_t c, int wid, int lane) {
-  const int64_t t = c / A.cpt;
-  const int k = (int)(c - t * A.cpt) * kChunkRows + kWaveRows * wid + lane;
-  int32_t v = -1;
-  if (lane < kWaveRows && k < A.topk) v = A.idx[t * A.topk + k];
-  return v;
+// Buffer resource over [base, base + bytes): raw byte addressing; an offset at or past
+// `bytes` reads as zero without a memory access.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;   // 32-bit data format, no swizzle
+  return r;
 }
 
-// Fetch this wave's 16 rows of chunk c into registers.  NVFP4 rows come from the pool at
-// their list index; FP8 rows (staged variant) sit at their list position.
-template <bool kFp8>
-__device__ __forceinline__ void issue(const DecodeArgs& A, int64_t c, int32_t idxv, Stage<kFp8>& S,
-                                      int wid, int lane) {
-  using F = Fmt<kFp8>;
-  S.idx = idxv;
-  const uint8_t* src = (const uint8_t*)A.rows;
-  const int64_t t = c / A.cpt;
-  const int64_t entry0 = t * A.topk + (c - t * A.cpt) * kChunkRows + kWaveRows * wid;
-#pragma unroll
-  for (int k = 0; k < F::kLoads; k++) {
-    const int p = 64 * k + lane;
-    const int r = p / F::kPiecesPerRow;                 // wave row of this piece
-    const int off = (p - F::kPiecesPerRow * r) * 16;
-    const int32_t row = __shfl(idxv, r & 15);
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (p < F::kWavePieces && row_valid(row, A.pool_rows)) {
-      const int64_t base = kFp8 ? (entry0 + r) * (int64_t)kHeadDim : (int64_t)row * kRowBytes;
-      v = *(const u32x4*)(src + base + off);
-    }
-    S.v[k] = v;
-  }
+// LDS DMA: lane l's 16 (4) bytes at buffer offset voff land at LDS byte lds + 16*l (4*l).
+// Issued as inline assembly so the compiler neither waits for nor reorders around them
+// implicitly; every consumer waits with an explicit vmcnt.
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rs)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(i32x4 rs, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rs)
+               : "memory", "m0");
 }
 
-template <bool kFp8>
-__device__ __forceinline__ void commit(const Stage<kFp8>& S, SMLA_LDS uint8_t* slot, int wid, int lane) {
-  using F = Fmt<kFp8>;
-  SMLA_LDS uint8_t* base = slot + wid * (kWaveRows * F::kRB);
-#pragma unroll
-  for (int k = 0; k < F::kLoads; k++) {
-    const int p = 64 * k + lane;
-    if (p < F::kWavePieces) lds_store<u32x4>(base + 16 * p, S.v[k]);
-  }
+// s_waitcnt vmcnt(N): vector memory operations complete in issue order, so this waits
+// for everything but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool kFp8>
-__device__ __forceinline__ uint64_t valid_mask(const DecodeArgs& A, const Stage<kFp8>& S, int lane) {
-  return __ballot(lane < kWaveRows && row_valid(S.idx, A.pool_rows));
+// LDS byte address of p (wave-uniform: DMA destinations go through m0).
+__device__ __forceinline__ uint32_t lds_addr(const SMLA_LDS void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
 __device__ __forceinline__ u32x2 lds_read_tr8(const SMLA_LDS void* p) {
@@ -134,283 +160,458 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const SMLA_LDS void* p) {
   return u32x2{(uint32_t)v.x, (uint32_t)v.y};
 }
 
-// Query tile of token t for head group hg: 16 heads x 576 fp16, fetched by the whole
-// workgroup (thread tid takes pieces tid, tid+256, ...).
-struct QStage {
-  u32x4 v[kQLoads];
+// Sum of eight fp16 values in fp32.
+__device__ __forceinline__ float sum8(f16x8 v) {
+  const f16x2 one = f16x2{(f16)1.0f, (f16)1.0f};
+  float s = __builtin_amdgcn_fdot2(f16x2{v[0], v[1]}, one, 0.0f, false);
+  s = __builtin_amdgcn_fdot2(f16x2{v[2], v[3]}, one, s, false);
+  s = __builtin_amdgcn_fdot2(f16x2{v[4], v[5]}, one, s, false);
+  return __builtin_amdgcn_fdot2(f16x2{v[6], v[7]}, one, s, false);
+}
+
+// Tile cursor: flat tile c -> token t and tile ci within the token, advanced one at a time.
+struct Cursor {
+  int64_t c;
+  int64_t t;
+  int32_t ci;
+  __device__ void init(int64_t c0, int32_t cpt) {
+    c = c0;
+    t = c0 / cpt;
+    ci = (int32_t)(c0 - t * cpt);
+  }
+  __device__ void next(int32_t cpt) {
+    c++;
+    if (++ci == cpt) {
+      ci = 0;
+      t++;
+    }
+  }
 };
 
-__device__ __forceinline__ void issue_q(const DecodeArgs& A, int64_t t, int hg, QStage& Q) {
-  const int tid = threadIdx.x;
-  const uint8_t* base = (const uint8_t*)A.q + ((t * A.H + (int64_t)kHeadGroup * hg) * kHeadDim) * 2;
+template <int NG>
+struct QReg {
+  f16x8 v[NG][18];   // B operand of QK step k: features 128g+8k.. (k < 16), 512+16g+8(k-16)..
+};
+
+// Query registers of token t for lane (head r16, group g): heads head0 + 16j + r16.
+template <int NG>
+__device__ __forceinline__ void load_q(const DecodeArgs& A, int64_t t, int head0, int r16, int g,
+                                       QReg<NG>& Q) {
 #pragma unroll
-  for (int k = 0; k < kQLoads; k++) {
-    const int p = 256 * k + tid;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (p < kQPieces) v = *(const u32x4*)(base + 16 * p);   // heads are contiguous in q
-    Q.v[k] = v;
+  for (int j = 0; j < NG; j++) {
+    const f16* base = (const f16*)A.q + ((t * A.H + head0 + kHeadGroup * j + r16) * kHeadDim);
+#pragma unroll
+    for (int k = 0; k < 16; k++) Q.v[j][k] = *(const f16x8*)(base + 128 * g + 8 * k);
+    Q.v[j][16] = *(const f16x8*)(base + kLatent + 16 * g);
+    Q.v[j][17] = *(const f16x8*)(base + kLatent + 16 * g + 8);
   }
 }
 
-__device__ __forceinline__ void commit_q(const QStage& Q, f16 (*qs)[kQStride]) {
-  const int tid = threadIdx.x;
+// Query registers from the staging area (layout of QFmt).
+template <int NG>
+__device__ __forceinline__ void read_q(const SMLA_LDS uint8_t* qs, int r16, int g, QReg<NG>& Q) {
 #pragma unroll
-  for (int k = 0; k < kQLoads; k++) {
-    const int p = 256 * k + tid;
-    if (p < kQPieces) {
-      const int h = p / (kHeadDim * 2 / 16), off = (p - h * (kHeadDim * 2 / 16)) * 8;
-      lds_store<u32x4>(&qs[h][off], Q.v[k]);
-    }
+  for (int j = 0; j < NG; j++) {
+    const SMLA_LDS uint8_t* h = qs + (kHeadGroup * j + r16) * 1168;
+#pragma unroll
+    for (int k = 0; k < 16; k++) Q.v[j][k] = lds_load<f16x8>(h + 16 * (16 * g + k));
+    Q.v[j][16] = lds_load<f16x8>(h + 16 * (64 + 2 * g));
+    Q.v[j][17] = lds_load<f16x8>(h + 16 * (65 + 2 * g));
   }
 }
 
 }  // namespace
 
-template <bool kFp8>
-__global__ __launch_bounds__(256, kFp8 ? 1 : 2) void sparse_mla_decode_kernel(DecodeArgs A) {
-  using F = Fmt<kFp8>;
-  __shared__ Smem<kFp8> sm;
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int hg = blockIdx.y;
+template <int NG, int ST, bool kFp8, int WPC>
+__global__ __launch_bounds__(256, WPC) void sparse_mla_decode_kernel(DecodeArgs A) {
+  using F = RowFmt<kFp8>;
+  constexpr int NH = kHeadGroup * NG;
+  constexpr int D = ST - 1;   // prefetch distance in tiles
+  constexpr int QB = kQBufs<NG, ST>;
+  static_assert(D == 1 || D == 2, "ring of two or three slots");
+  __shared__ Smem<NG, ST, kFp8> sm;
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r16 = lane & 15, g = lane >> 4;
+
+  // XCD-aware order: hardware deals block b to XCD b % 8; give each XCD a contiguous run
+  // of logical workgroups (the head blocks of one range, then neighbouring ranges).
+  const int nb = gridDim.x, b = blockIdx.x, xcd = b & 7, per = nb >> 3, rem = nb & 7;
+  const int L = xcd * per + min(xcd, rem) + (b >> 3);
+  const int w = L / A.HB, hb = L - w * A.HB;
+  const int64_t C = A.tiles;
   const int G = A.G;
-  // XCD-aware order: hardware deals block b to XCD b % 8; give each XCD a contiguous
-  // run of logical workgroups so that neighbouring ranges (same tokens) share an L2.
-  const int bx = blockIdx.x, xcd = bx & 7, G8 = G >> 3, Gr = G & 7;
-  const int w = xcd * G8 + min(xcd, Gr) + (bx >> 3);
-  const int64_t C = A.chunks;
+  const int cpt = A.cpt;
   const int64_t c_lo = wg_first_chunk(w, C, G), c_hi = wg_first_chunk(w + 1, C, G);
   const int n = (int)(c_hi - c_lo);
-  const int cpt = A.cpt;
-
-  SMLA_LDS uint8_t* ring0 = (SMLA_LDS uint8_t*)sm.ring[0];
-  SMLA_LDS uint8_t* ring1 = (SMLA_LDS uint8_t*)sm.ring[1];
-
-  // ---- prologue: chunks 0 and 1 in flight, chunk 0 in LDS
-  // Index lists run two chunks ahead of the row loads: loads complete in issue order, so
-  // waiting for an index load also waits for every load issued before it.
-  Stage<kFp8> s0, s1;
-  const int32_t idx0 = load_idx(A, c_lo, wid, lane);
-  const int32_t idx1 = (n > 1) ? load_idx(A, c_lo + 1, wid, lane) : -1;
-  int32_t idx_a = (n > 2) ? load_idx(A, c_lo + 2, wid, lane) : -1;   // chunk i+2 at step i
-  int32_t idx_b = (n > 3) ? load_idx(A, c_lo + 3, wid, lane) : -1;   // chunk i+3 at step i
-  issue(A, c_lo, idx0, s0, wid, lane);
-  if (n > 1) issue(A, c_lo + 1, idx1, s1, wid, lane);
-  QStage qst;
-  issue_q(A, c_lo / cpt, hg, qst);
-  uint64_t vm_cur = valid_mask(A, s0, lane);
-  commit(s0, ring0, wid, lane);
-  commit_q(qst, sm.qs);
-  __syncthreads();
-
-  f32x4 O[8];
-  float m_ref = -INFINITY, l_part = 0.0f;
-  int64_t pend0 = -1, pend1 = -1;   // tokens whose partials this workgroup merges (<= 2)
+  const int head0 = hb * NH;
   const float sl2 = A.scale_log2;
-  const int head = kHeadGroup * hg + r16;
 
-  auto step = [&](int i, Stage<kFp8>& freeS, Stage<kFp8>& nextS) {
-    const int64_t c = c_lo + i;
-    const int64_t t = c / cpt;
-    const int cin = (int)(c - t * cpt);
-    const bool seg_first = (i == 0) || (cin == 0);
-    const bool seg_last = (i == n - 1) || (cin == cpt - 1);
-    SMLA_LDS uint8_t* sb = (i & 1) ? ring1 : ring0;
-    if (seg_first) {
-#pragma unroll
-      for (int k = 0; k < 8; k++) O[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_ref = -INFINITY;
-      l_part = 0.0f;
-    }
-    // the next chunk starts a new token: fetch its query tile, committed after this chunk
-    const bool next_new_tok = (i + 1 < n) && (cin == cpt - 1);
-    if (next_new_tok) issue_q(A, t + 1, hg, qst);
-    // prefetch chunk i+2 into the free register set, index list of chunk i+4
-    if (i + 2 < n) {
-      issue(A, c + 2, idx_a, freeS, wid, lane);
-      idx_a = idx_b;
-      idx_b = (i + 4 < n) ? load_idx(A, c + 4, wid, lane) : -1;
-    }
+  const i32x4 rs_rows = make_rsrc(A.rows, A.rows_bytes);
+  const i32x4 rs_idx = make_rsrc(A.idx, A.idx_bytes);
+  const i32x4 rs_q = make_rsrc(A.q, A.q_bytes);
+  SMLA_LDS uint8_t* const ring = (SMLA_LDS uint8_t*)sm.ring;
+  SMLA_LDS int32_t* const idxbuf = (SMLA_LDS int32_t*)sm.idx;
 
-    // ---- QK^T for rows 16*wid + r16 (A operand), 16 heads (B operand)
-    const uint64_t vm = vm_cur;
-    {
-      const SMLA_LDS uint8_t* rp = sb + (kWaveRows * wid + r16) * F::kRB;
-      // B operand of step k: query features 128g+8k.. (k < 16) or 512+16g+8(k-16)..
-      auto qop = [&](int k) {
-        return lds_load<f16x8>(&sm.qs[r16][k < 16 ? 128 * g + 8 * k : kLatent + 16 * g + 8 * (k - 16)]);
-      };
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (!kFp8) {
-        u32x4 cw[4];
-#pragma unroll
-        for (int k = 0; k < 4; k++) cw[k] = lds_load<u32x4>(rp + 64 * g + 16 * k);
-        const u32x2 scb = lds_load<u32x2>(rp + kScaleOff + 8 * g);
-        const u32x4 rb = lds_load<u32x4>(rp + kRopeOff + 16 * g);
-        const f16x2 s01 = e4m3x2<false>(scb.x), s23 = e4m3x2<true>(scb.x);
-        const f16x2 s45 = e4m3x2<false>(scb.y), s67 = e4m3x2<true>(scb.y);
-        const f16 sf[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
-#pragma unroll
-        for (int k = 0; k < 16; k++) {
-          const f16 s = sf[k >> 1];
-          acc = mfma16x16x32(unpack8(cw[k >> 2][k & 3], f16x2{s, s}), qop(k), acc);
-          // keep the scheduler from hoisting every operand read ahead of the MFMA chain
-          if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
-        acc = mfma16x16x32(fp8x8(rb.x, rb.y), qop(16), acc);
-        acc = mfma16x16x32(fp8x8(rb.z, rb.w), qop(17), acc);
-        // scale table for PV: this wave's rows, empty rows scaled by zero
-        const bool rv = (vm >> r16) & 1;
-#pragma unroll
-        for (int j = 0; j < 8; j++) sm.sc[8 * g + j][kWaveRows * wid + r16] = rv ? sf[j] : (f16)0.0f;
-      } else {
-        // FP8 row: latent bytes 128g.. (16 steps of 8), rope bytes 512+16g..
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const u32x4 cw = lds_load<u32x4>(rp + 128 * g + 16 * k);
-          acc = mfma16x16x32(fp8x8(cw.x, cw.y), qop(2 * k), acc);
-          acc = mfma16x16x32(fp8x8(cw.z, cw.w), qop(2 * k + 1), acc);
-        }
-        const u32x4 rb = lds_load<u32x4>(rp + kLatent + 16 * g);
-        acc = mfma16x16x32(fp8x8(rb.x, rb.y), qop(16), acc);
-        acc = mfma16x16x32(fp8x8(rb.z, rb.w), qop(17), acc);
-      }
-
-      // acc[j] = score of row 16*wid + 4*g + j for head r16
-      float sl[4];
-#pragma unroll
-      for (int j = 0; j < 4; j++) sl[j] = ((vm >> (4 * g + j)) & 1) ? acc[j] * sl2 : -INFINITY;
-      float mx = fmaxf(fmaxf(sl[0], sl[1]), fmaxf(sl[2], sl[3]));
-      mx = wave_max_xor16_32(mx);
-      if (lane < kHeadGroup) sm.xmax[wid][lane] = mx;
-      __syncthreads();
-      const float cmax = fmaxf(fmaxf(sm.xmax[0][r16], sm.xmax[1][r16]),
-                               fmaxf(sm.xmax[2][r16], sm.xmax[3][r16]));
-      if (cmax > m_ref + kRescaleSlack) {
-        const float alpha = exp2f(m_ref - cmax);   // 0 when m_ref = -inf
-#pragma unroll
-        for (int k = 0; k < 8; k++) O[k] *= alpha;
-        l_part *= alpha;
-        m_ref = cmax;
-      }
-      f16 p16[4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const float pv = (sl[j] == -INFINITY) ? 0.0f : exp2f(sl[j] - m_ref);
-        p16[j] = (f16)pv;
-        psum += (float)p16[j];
-      }
-      l_part += psum;
-      lds_store<f16x4>(&sm.pb[r16][kWaveRows * wid + 4 * g], f16x4{p16[0], p16[1], p16[2], p16[3]});
+  // DMA of this wave's 16 index entries of tile cur (relative index i) into idx[i & 1][wid].
+  auto issue_idx = [&](const Cursor& cur, int i) {
+    const int k = cur.ci * kTileRows + kWR * wid + lane;
+    const bool ok = cur.c < c_hi && k < A.topk;
+    const uint32_t voff = ok ? (uint32_t)((cur.t * A.topk + k) * 4) : kOOB;
+    if (lane < kWR) dma4(rs_idx, voff, lds_addr(idxbuf + ((i & 1) * kWaves + wid) * kWR));
+  };
+  // DMA of this wave's share (instructions wid, wid+4, ...) of the query rows of token t.
+  auto issue_q = [&](int64_t t) {
+    const uint32_t lds0 = lds_addr((SMLA_LDS uint8_t*)sm.qst[t % QB]);
+    for (int kk = wid; kk < QFmt<NG>::kLoads; kk += kWaves) {
+      const int sl = 64 * kk + lane, h = sl / 73, p = sl - 73 * h;
+      const bool ok = h < NH && p < 72;
+      const uint32_t voff = ok ? (uint32_t)((t * A.H + head0 + h) * (int64_t)(2 * kHeadDim)) + 16u * p : kOOB;
+      dma16(rs_q, voff, lds0 + 1024u * kk);
     }
-    __syncthreads();
-
-    // ---- PV: O^T[16*tau + feature][head] += V^T P^T over the chunk's 64 rows
-    {
-      const f16x8 bop0 = lds_load<f16x8>(&sm.pb[r16][8 * g]);
-      const f16x8 bop1 = lds_load<f16x8>(&sm.pb[r16][32 + 8 * g]);
-      if constexpr (!kFp8) {
-        // 4-bit transpose read: lane s of group g supplies row 8g+s (s < 8) or 32+8g+s-8;
-        // dword 0 then holds rows 8g..8g+7 and dword 1 rows 32+8g.. of feature 16*tau+r16.
-        const int trow = (r16 < 8) ? (8 * g + r16) : (32 + 8 * g + r16 - 8);
-        const SMLA_LDS uint8_t* tp = sb + trow * kRowBytes;
+  };
+  // DMA of this wave's rows of tile cur into ring slot i % ST (its index entries must have
+  // landed), preceded by the query of its token when the tile starts a token (i >= 1).
+  // The slot was last read by the PV of tile i - ST, which every wave finished before the
+  // barrier of tile i - D that precedes this call.  Returns the mask of valid rows (bit r =
+  // wave row r).
+  auto issue_rows = [&](const Cursor& cur, int i) -> uint32_t {
+    if (i >= 1 && cur.ci == 0 && cur.c < c_hi) issue_q(cur.t);
+    const int k = cur.ci * kTileRows + kWR * wid + r16;
+    const int32_t v = idxbuf[((i & 1) * kWaves + wid) * kWR + r16];
+    const bool ok = cur.c < c_hi && k < A.topk && row_valid(v, A.pool_rows);
+    uint32_t base;
+    if constexpr (kFp8)
+      base = (uint32_t)((cur.t * A.topk + k) * (int64_t)kHeadDim);
+    else
+      base = (uint32_t)v * (uint32_t)kRowBytes;
+    const uint32_t lds0 = lds_addr(ring + (i % ST) * F::kSlot + wid * F::kPortion);
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const int tau = 8 * wid + k;
-          const u32x2 d = lds_read_tr4(tp + 8 * tau);
-          const f16x8 sc0 = lds_load<f16x8>(&sm.sc[tau][8 * g]);
-          const f16x8 sc1 = lds_load<f16x8>(&sm.sc[tau][32 + 8 * g]);
-          O[k] = mfma16x16x32(unpack8_pairs(d.x, sc0), bop0, O[k]);
-          O[k] = mfma16x16x32(unpack8_pairs(d.y, sc1), bop1, O[k]);
-        }
-      } else {
-        // 8-bit transpose read: lane s of group g supplies 8 bytes of row (8g + s/2) at
-        // feature offset 8*(s%2); lane i receives feature 16*tau+i of rows 8g..8g+7.
-        const SMLA_LDS uint8_t* tp0 = sb + (8 * g + (r16 >> 1)) * kHeadDim + 8 * (r16 & 1);
-        const SMLA_LDS uint8_t* tp1 = tp0 + 32 * kHeadDim;
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const int tau = 8 * wid + k;
-          const u32x2 d0 = lds_read_tr8(tp0 + 16 * tau);
-          const u32x2 d1 = lds_read_tr8(tp1 + 16 * tau);
-          O[k] = mfma16x16x32(fp8x8(d0.x, d0.y), bop0, O[k]);
-          O[k] = mfma16x16x32(fp8x8(d1.x, d1.y), bop1, O[k]);
-        }
-      }
+    for (int kk = 0; kk < F::kLoads; kk++) {
+      const int piece = 4 * kk + g;
+      const uint32_t voff = ok ? base + 16u * piece : kOOB;
+      // the last instruction of an NVFP4 row set covers pieces 20..23 of which 22 and 23
+      // do not exist: those lanes stay idle (the instruction is still issued)
+      if (4 * kk + 3 < F::kPieces || piece < F::kPieces) dma16(rs_rows, voff, lds0 + 1024u * kk);
     }
-
-    // ---- stage the next chunk into the other LDS slot (its previous chunk is consumed)
-    if (i + 1 < n) {
-      vm_cur = valid_mask(A, nextS, lane);
-      commit(nextS, (i & 1) ? ring0 : ring1, wid, lane);
-    }
-    if (next_new_tok) commit_q(qst, sm.qs);   // every wave is past its QK of this chunk
-
-    // ---- epilogue of a token segment
-    if (seg_last) {
-      const float lw = wave_sum_xor16_32(l_part);
-      if (lane < kHeadGroup) sm.lsum[wid][lane] = lw;
-      __syncthreads();
-      const float L = sm.lsum[0][r16] + sm.lsum[1][r16] + sm.lsum[2][r16] + sm.lsum[3][r16];
-      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      const float lse_nat = L > 0.0f ? (m_ref + log2f(L)) * kLn2 : -INFINITY;
-      const int64_t tok0 = t * cpt;
-      const bool full = (c_lo <= tok0) && (c_hi >= tok0 + cpt);
-      if (full) {
-        f16* op = (f16*)A.out + ((int64_t)t * A.H + head) * kLatent;
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const f32x4 v = O[k] * inv;
-          *(f16x4*)(op + 16 * (8 * wid + k) + 4 * g) = f16x4{(f16)v.x, (f16)v.y, (f16)v.z, (f16)v.w};
-        }
-        if (wid == 0 && lane < kHeadGroup) A.lse[(int64_t)t * A.H + head] = lse_nat;
-      } else {
-        const int64_t slot = ((int64_t)hg * G + w) * A.max_seg + (t - c_lo / cpt);
-        float* po = A.part_o + (slot * kHeadGroup + r16) * kLatent;
-#pragma unroll
-        for (int k = 0; k < 8; k++) store_coherent(po + 16 * (8 * wid + k) + 4 * g, O[k] * inv);
-        if (wid == 0 && lane < kHeadGroup) store_coherent(A.part_lse + slot * kHeadGroup + r16, lse_nat);
-        // publish (stores complete), count, and let the last workgroup of this token merge
-        const int64_t w_lo = wg_of_chunk(tok0, C, G), w_hi = wg_of_chunk(tok0 + cpt - 1, C, G);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (threadIdx.x == 0) {
-          int32_t* cnt = A.counters + (int64_t)hg * A.T + t;
-          const int old = atomicAdd(cnt, 1);
-          const int last = (old == (int)(w_hi - w_lo));
-          if (last) atomicExch(cnt, 0);
-          sm.flag = last;
-        }
-        __syncthreads();
-        if (sm.flag) {   // merged after the main loop, outside the unrolled body
-          if (pend0 < 0) pend0 = t; else pend1 = t;
-        }
-      }
-    }
-    __syncthreads();
+    return (uint32_t)__ballot(ok && g == 0) & 0xFFFFu;
   };
 
-  for (int i = 0; i < n; i += 2) {
-    step(i, s0, s1);
-    if (i + 1 < n) step(i + 1, s1, s0);
+  // ---- prologue: query of the first token (into registers); index entries of tiles 0, 1;
+  // then rows(d) and idx(d+2) for d < D.  From here on the vector memory operations are
+  // issued in the order  ..., [q(c)], rows(c), idx(c+2), [q(c+1)], rows(c+1), ...  where
+  // q(c) is the query DMA of a token whose first tile c lies in the range (c >= 1).  With
+  // D = 2 the rows of tile i+2 are issued after the barrier of tile i; with D = 1 the rows
+  // of tile i+1 are issued at the start of tile i, after a barrier of their own.
+  QReg<NG> Q;
+  Cursor cr, cx;   // cursors of the next row DMA (tile i+D) and index DMA (tile i+D+2)
+  cr.init(c_lo, cpt);
+  cx.init(c_lo, cpt);
+  load_q<NG>(A, cr.t, head0, r16, g, Q);
+  issue_idx(cx, 0);
+  cx.next(cpt);
+  issue_idx(cx, 1);
+  cx.next(cpt);
+  wait_vm<0>();
+  uint32_t vmq[D + 1];   // valid-row masks of tiles i .. i+D
+#pragma unroll
+  for (int d = 0; d < D; d++) {
+    vmq[d] = issue_rows(cr, d);
+    cr.next(cpt);
+    issue_idx(cx, d + 2);
+    cx.next(cpt);
+  }
+  vmq[D] = 0;
+
+  f32x4 O[NG][8];
+  float m_ref[NG], l_acc[NG];
+#pragma unroll
+  for (int j = 0; j < NG; j++) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) O[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref[j] = -INFINITY;
+    l_acc[j] = 0.0f;
+  }
+  Cursor cu;   // tile being computed
+  cu.init(c_lo, cpt);
+  const int64_t t_first = cu.t;
+  int64_t pend_t[2] = {-1, -1};   // tokens this range wrote partials for (first, last)
+
+  for (int i = 0; i < n; i++) {
+    const int par = i & 1;
+    SMLA_LDS uint8_t* const slot = ring + (i % ST) * F::kSlot;
+    if constexpr (D == 2) {
+      // rows(i), idx(i+2) and a query DMA issued before rows(i+1) have landed; rows(i+1)
+      // and idx(i+3) may still be in flight
+      wait_vm<F::kLoads + 1>();
+      // first tile of a later token: every wave waited for its share of the staged query
+      // before the previous tile's barrier
+      if (i > 0 && cu.ci == 0) read_q<NG>((const SMLA_LDS uint8_t*)sm.qst[cu.t % QB], r16, g, Q);
+    } else {
+      wait_vm<1>();   // rows(i) and a query DMA before them landed; idx(i+2) may be in flight
+      // every wave's rows of tile i (and share of a staged query) have landed, and every
+      // wave has finished the PV of tile i-1: the other slot is free for tile i+1, whose
+      // rows are fetched now, a whole tile of work ahead of their use
+      __syncthreads();
+      vmq[1] = issue_rows(cr, i + 1);
+      cr.next(cpt);
+      issue_idx(cx, i + 3);
+      cx.next(cpt);
+      if (i > 0 && cu.ci == 0) read_q<NG>((const SMLA_LDS uint8_t*)sm.qst[cu.t % QB], r16, g, Q);
+    }
+    const uint32_t vm = vmq[0];
+
+    // ---- QK^T: rows 16*wid + r16 of the tile (A operand) against the block's heads
+    {
+      const SMLA_LDS uint8_t* por = slot + wid * F::kPortion;
+      f32x4 acc[2][NG];
+#pragma unroll
+      for (int j = 0; j < NG; j++) acc[0][j] = acc[1][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (vm != 0) {
+        if constexpr (!kFp8) {
+          u32x4 cw[4];
+#pragma unroll
+          for (int k = 0; k < 4; k++) cw[k] = lds_load<u32x4>(por + 256 * (4 * g + k) + 16 * r16);
+          const u32x2 scb = lds_load<u32x2>(por + 256 * (16 + (g >> 1)) + 16 * r16 + 8 * (g & 1));
+          const u32x4 rb = lds_load<u32x4>(por + 256 * (18 + g) + 16 * r16);
+          const f16x2 s01 = e4m3x2<false>(scb.x), s23 = e4m3x2<true>(scb.x);
+          const f16x2 s45 = e4m3x2<false>(scb.y), s67 = e4m3x2<true>(scb.y);
+          const f16 sf[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
+#pragma unroll
+          for (int k = 0; k < 16; k++) {
+            const f16 s = sf[k >> 1];
+            const f16x8 a = unpack8(cw[k >> 2][k & 3], f16x2{s, s});
+#pragma unroll
+            for (int j = 0; j < NG; j++) acc[k & 1][j] = mfma16x16x32(a, Q.v[j][k], acc[k & 1][j]);
+          }
+          const f16x8 r0 = fp8x8(rb.x, rb.y), r1 = fp8x8(rb.z, rb.w);
+#pragma unroll
+          for (int j = 0; j < NG; j++) {
+            acc[0][j] = mfma16x16x32(r0, Q.v[j][16], acc[0][j]);
+            acc[1][j] = mfma16x16x32(r1, Q.v[j][17], acc[1][j]);
+          }
+          // PV scale table: this wave's rows, empty rows scaled by zero
+          const bool rv = (vm >> r16) & 1;
+          const int row = kWR * wid + r16;
+#pragma unroll
+          for (int jj = 0; jj < 8; jj++) sm.sc[par][8 * g + jj][row] = rv ? sf[jj] : (f16)0.0f;
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; k++) {
+            const u32x4 cw = lds_load<u32x4>(por + 256 * (8 * g + k) + 16 * r16);
+            const f16x8 a0 = fp8x8(cw.x, cw.y), a1 = fp8x8(cw.z, cw.w);
+#pragma unroll
+            for (int j = 0; j < NG; j++) {
+              acc[0][j] = mfma16x16x32(a0, Q.v[j][2 * k], acc[0][j]);
+              acc[1][j] = mfma16x16x32(a1, Q.v[j][2 * k + 1], acc[1][j]);
+            }
+          }
+          const u32x4 rb = lds_load<u32x4>(por + 256 * (32 + g) + 16 * r16);
+          const f16x8 r0 = fp8x8(rb.x, rb.y), r1 = fp8x8(rb.z, rb.w);
+#pragma unroll
+          for (int j = 0; j < NG; j++) {
+            acc[0][j] = mfma16x16x32(r0, Q.v[j][16], acc[0][j]);
+            acc[1][j] = mfma16x16x32(r1, Q.v[j][17], acc[1][j]);
+          }
+        }
+      } else if constexpr (!kFp8) {
+#pragma unroll
+        for (int jj = 0; jj < 8; jj++) sm.sc[par][8 * g + jj][kWR * wid + r16] = (f16)0.0f;
+      }
+
+      // acc[.][j][jj] = score of tile row 16*wid + 4g + jj for head 16j + r16.  The wave's
+      // reference for a head is the shared one unless its rows exceed that by more than
+      // the slack, then its own maximum.
+      bool raised = false;
+      const int rbase = kWR * wid + 4 * g;
+#pragma unroll
+      for (int j = 0; j < NG; j++) {
+        const f32x4 a = acc[0][j] + acc[1][j];
+        float s[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) s[jj] = ((vm >> (4 * g + jj)) & 1) ? a[jj] * sl2 : -INFINITY;
+        const float mx = wave_max_xor16_32(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+        const float ref = (mx > m_ref[j] + kSlack) ? mx : m_ref[j];
+        raised |= ref != m_ref[j];
+        f16 p[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+          p[jj] = (s[jj] == -INFINITY) ? (f16)0.0f : (f16)__builtin_amdgcn_exp2f(s[jj] - ref);
+        lds_store<f16x4>(&sm.pb[par][kHeadGroup * j + r16][rbase], f16x4{p[0], p[1], p[2], p[3]});
+        if (g == 0) sm.wref[par][wid][kHeadGroup * j + r16] = ref;
+      }
+      const bool wave_raised = __ballot(raised) != 0;
+      if (lane == 0) sm.wflag[par][wid] = (wave_raised ? 1 : 0) | (vm != 0 ? 2 : 0);
+    }
+
+    __syncthreads();
+
+    // ---- prefetch (distance two): rows of tile i+2 into the slot the PV of tile i-1
+    // released, index entries of tile i+4 (idx(i+2) landed with an earlier wait)
+    if constexpr (D == 2) {
+      vmq[2] = issue_rows(cr, i + 2);
+      cr.next(cpt);
+      issue_idx(cx, i + 4);
+      cx.next(cpt);
+    }
+
+    // ---- probabilities of the whole tile for this lane's PV operand (rows 8g..8g+7 from
+    // wave g/2, rows 32+8g.. from wave 2+g/2)
+    const int fl = sm.wflag[par][0] | sm.wflag[par][1] | sm.wflag[par][2] | sm.wflag[par][3];
+    f16x8 bop[NG][2];
+#pragma unroll
+    for (int j = 0; j < NG; j++) {
+      bop[j][0] = lds_load<f16x8>(&sm.pb[par][kHeadGroup * j + r16][8 * g]);
+      bop[j][1] = lds_load<f16x8>(&sm.pb[par][kHeadGroup * j + r16][32 + 8 * g]);
+    }
+    if (fl & 1) {
+      // a wave raised its reference: the new shared reference is the largest one used;
+      // rescale the accumulator and the probabilities computed against a smaller one
+#pragma unroll
+      for (int j = 0; j < NG; j++) {
+        const int h = kHeadGroup * j + r16;
+        const float r0 = sm.wref[par][0][h], r1 = sm.wref[par][1][h];
+        const float r2 = sm.wref[par][2][h], r3 = sm.wref[par][3][h];
+        const float mnew = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+        if (mnew != m_ref[j]) {
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[j] - mnew);   // 0 if m_ref = -inf
+#pragma unroll
+          for (int k = 0; k < 8; k++) O[j][k] *= alpha;
+          l_acc[j] *= alpha;
+          m_ref[j] = mnew;
+        }
+        const float f0 = (g >> 1) == 0 ? r0 : r1, f1 = (g >> 1) == 0 ? r2 : r3;
+        if (f0 != mnew) {
+          const f16 e = (f16)__builtin_amdgcn_exp2f(f0 - mnew);
+          bop[j][0] *= f16x8{e, e, e, e, e, e, e, e};
+        }
+        if (f1 != mnew) {
+          const f16 e = (f16)__builtin_amdgcn_exp2f(f1 - mnew);
+          bop[j][1] *= f16x8{e, e, e, e, e, e, e, e};
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NG; j++) l_acc[j] += sum8(bop[j][0]) + sum8(bop[j][1]);
+
+    // ---- PV: O^T[16*tau + feature][head] += V^T P^T over the tile's 64 rows
+    if (fl & 2) {
+      if constexpr (!kFp8) {
+        // 4-bit transpose read: lane s of group g supplies tile row 8g+s (s < 8) or
+        // 32+8g+s-8; dword 0 then holds rows 8g..8g+7 and dword 1 rows 32+8g.. of
+        // feature 16*tau + r16.
+        const int R = (r16 < 8) ? (8 * g + r16) : (32 + 8 * g + r16 - 8);
+        const SMLA_LDS uint8_t* tb = slot + (R >> 4) * F::kPortion + 16 * (R & 15);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          const int tau = 8 * wid + k;
+          const u32x2 d = lds_read_tr4(tb + 256 * (tau >> 1) + 8 * (tau & 1));
+          const f16x8 sc0 = lds_load<f16x8>(&sm.sc[par][tau][8 * g]);
+          const f16x8 sc1 = lds_load<f16x8>(&sm.sc[par][tau][32 + 8 * g]);
+          const f16x8 a0 = unpack8_pairs(d.x, sc0), a1 = unpack8_pairs(d.y, sc1);
+#pragma unroll
+          for (int j = 0; j < NG; j++) {
+            O[j][k] = mfma16x16x32(a0, bop[j][0], O[j][k]);
+            O[j][k] = mfma16x16x32(a1, bop[j][1], O[j][k]);
+          }
+        }
+      } else {
+        // 8-bit transpose read: lane s of group g supplies 8 bytes of tile row 8g + s/2
+        // at feature offset 8*(s%2); lane i receives feature 16*tau+i of rows 8g..8g+7.
+        const int R0 = 8 * g + (r16 >> 1), R1 = R0 + 32;
+        const SMLA_LDS uint8_t* tb0 = slot + (R0 >> 4) * F::kPortion + 16 * (R0 & 15) + 8 * (r16 & 1);
+        const SMLA_LDS uint8_t* tb1 = slot + (R1 >> 4) * F::kPortion + 16 * (R1 & 15) + 8 * (r16 & 1);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          const int tau = 8 * wid + k;
+          const u32x2 d0 = lds_read_tr8(tb0 + 256 * tau);
+          const u32x2 d1 = lds_read_tr8(tb1 + 256 * tau);
+          const f16x8 a0 = fp8x8(d0.x, d0.y), a1 = fp8x8(d1.x, d1.y);
+#pragma unroll
+          for (int j = 0; j < NG; j++) {
+            O[j][k] = mfma16x16x32(a0, bop[j][0], O[j][k]);
+            O[j][k] = mfma16x16x32(a1, bop[j][1], O[j][k]);
+          }
+        }
+      }
+    }
+
+    // ---- end of a token segment: write the output or a partial, then start afresh
+    if (i == n - 1 || cu.ci == cpt - 1) {
+      const int64_t t = cu.t;
+      const int64_t tok0 = t * cpt;
+      const bool full = (c_lo <= tok0) && (c_hi >= tok0 + cpt);
+      const int seg = (t == t_first) ? 0 : 1;
+      const int64_t slot_id = ((int64_t)hb * G + w) * 2 + seg;
+#pragma unroll
+      for (int j = 0; j < NG; j++) {
+        const float Ls = wave_sum_xor16_32(l_acc[j]);
+        const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+        const float lse_nat = Ls > 0.0f ? (m_ref[j] + log2f(Ls)) * kLn2 : -INFINITY;
+        const int hl = kHeadGroup * j + r16;   // head within the block
+        if (full) {
+          f16* op = (f16*)A.out + (t * A.H + head0 + hl) * kLatent;
+#pragma unroll
+          for (int k = 0; k < 8; k++) {
+            const f32x4 v = O[j][k] * inv;
+            *(f16x4*)(op + 16 * (8 * wid + k) + 4 * g) = f16x4{(f16)v.x, (f16)v.y, (f16)v.z, (f16)v.w};
+          }
+          if (wid == 0 && g == 0) A.lse[t * A.H + head0 + hl] = lse_nat;
+        } else {
+          float* po = A.part_o + (slot_id * NH + hl) * kLatent;
+#pragma unroll
+          for (int k = 0; k < 8; k++) store_coherent(po + 16 * (8 * wid + k) + 4 * g, O[j][k] * inv);
+          if (wid == 0 && g == 0) store_coherent(A.part_lse + slot_id * NH + hl, lse_nat);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) O[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_ref[j] = -INFINITY;
+        l_acc[j] = 0.0f;
+      }
+      if (!full) pend_t[seg] = t;
+    }
+    cu.next(cpt);
+#pragma unroll
+    for (int d = 0; d < D; d++) vmq[d] = vmq[d + 1];
   }
 
-  // ---- log-sum-exp merge of the tokens this workgroup finished last
-  for (int k = 0; k < 2; k++) {
-    const int64_t t = k == 0 ? pend0 : pend1;
+  // ---- publish this range's partials (all stores complete), and merge the tokens whose
+  // last range this is
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t ws_o = merge_rsrc(A.part_o, A.part_o_bytes);
+  const __amdgpu_buffer_rsrc_t ws_l = merge_rsrc(A.part_lse, A.part_lse_bytes);
+  float* const scratch = (float*)sm.ring;   // the ring is idle from here on
+#pragma unroll
+  for (int seg = 0; seg < 2; seg++) {
+    const int64_t t = pend_t[seg];
     if (t < 0) continue;
     const int64_t tok0 = t * cpt;
     const int64_t w_lo = wg_of_chunk(tok0, C, G), w_hi = wg_of_chunk(tok0 + cpt - 1, C, G);
-    auto part = [&](int s, const float** o, const float** l) {
-      const int64_t ws = w_lo + s;
-      const int64_t sl = ((int64_t)hg * G + ws) * A.max_seg + (t - wg_first_chunk(ws, C, G) / cpt);
-      *o = A.part_o + sl * kHeadGroup * kLatent;
-      *l = A.part_lse + sl * kHeadGroup;
+    if (tid == 0) {
+      int32_t* cnt = A.counters + (int64_t)hb * A.T + t;
+      const int old = atomicAdd(cnt, 1);
+      const int last = (old == (int)(w_hi - w_lo));
+      if (last) atomicExch(cnt, 0);
+      sm.flag = last;
+    }
+    __syncthreads();
+    const int last = sm.flag;
+    __syncthreads();
+    if (!last) continue;
+    // split s of token t is range w_lo + s.  Every range after w_lo starts inside the
+    // token, so t is its first token (slot 0); range w_lo holds t in slot 1 exactly when
+    // it starts before the token.
+    const uint32_t sl0 = (uint32_t)(((int64_t)hb * G + w_lo) * 2);
+    const uint32_t seg0 = (wg_first_chunk(w_lo, C, G) < tok0) ? 1u : 0u;
+    auto part = [&](int s, uint32_t* o_off, uint32_t* l_off) {
+      const uint32_t sl = sl0 + 2u * (uint32_t)s + (s == 0 ? seg0 : 0u);
+      *o_off = sl * (uint32_t)(NH * kLatent * 4);
+      *l_off = sl * (uint32_t)(NH * 4);
     };
-    lse_merge16<true>((int)(w_hi - w_lo + 1), part,
-                (f16*)A.out + ((int64_t)t * A.H + kHeadGroup * hg) * kLatent, kLatent,
-                A.lse + (int64_t)t * A.H + kHeadGroup * hg);
+    lse_merge<NH, true>((int)(w_hi - w_lo + 1), ws_o, ws_l, part,
+                        (f16*)A.out + (t * A.H + head0) * kLatent, A.lse + t * A.H + head0, scratch);
+    __syncthreads();
   }
 }
 
@@ -419,24 +620,37 @@ __global__ __launch_bounds__(256) void sparse_mla_combine_kernel(const float* __
                                                                  int32_t T, int32_t S, int32_t H,
                                                                  f16* __restrict__ out,
                                                                  float* __restrict__ lse) {
+  __shared__ float scratch[2048];
   const int t = blockIdx.x, hg = blockIdx.y;
-  auto part = [&](int s, const float** o, const float** l) {
-    const int64_t base = ((int64_t)t * S + s) * H + kHeadGroup * hg;
-    *o = part_o + base * kLatent;
-    *l = part_lse + base;
+  const __amdgpu_buffer_rsrc_t ro = merge_rsrc(part_o, (uint32_t)((uint64_t)T * S * H * kLatent * 4));
+  const __amdgpu_buffer_rsrc_t rl = merge_rsrc(part_lse, (uint32_t)((uint64_t)T * S * H * 4));
+  auto part = [&](int s, uint32_t* o_off, uint32_t* l_off) {
+    const uint32_t base = (uint32_t)(((int64_t)t * S + s) * H + kHeadGroup * hg);
+    *o_off = base * (uint32_t)(kLatent * 4);
+    *l_off = base * 4u;
   };
-  lse_merge16<false>(S, part, out + ((int64_t)t * H + kHeadGroup * hg) * kLatent, kLatent,
-              lse + (int64_t)t * H + kHeadGroup * hg);
+  lse_merge<kHeadGroup, false>(S, ro, rl, part, out + ((int64_t)t * H + kHeadGroup * hg) * kLatent,
+                               lse + (int64_t)t * H + kHeadGroup * hg, scratch);
 }
 
-hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(sparse_mla_decode_kernel<false>, dim3(a.G, a.H / kHeadGroup), dim3(256), 0, s, a);
+namespace {
+template <int NG, int ST, bool kFp8, int WPC>
+hipError_t launch_variant(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((sparse_mla_decode_kernel<NG, ST, kFp8, WPC>), dim3(a.G * a.HB), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+}  // namespace
+
+int decode_wgs_per_cu(bool fp8rows, int32_t NG) { return (!fp8rows && NG == 1) ? 2 : 1; }
+
+hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s) {
+  return (a.HB * 2 * kHeadGroup == a.H) ? launch_variant<2, 3, false, 1>(a, s)
+                                        : launch_variant<1, 2, false, 2>(a, s);
 }
 
 hipError_t launch_decode_fp8rows(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(sparse_mla_decode_kernel<true>, dim3(a.G, a.H / kHeadGroup), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return (a.HB * 2 * kHeadGroup == a.H) ? launch_variant<2, 2, true, 1>(a, s)
+                                        : launch_variant<1, 2, true, 1>(a, s);
 }
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t T, int32_t S,

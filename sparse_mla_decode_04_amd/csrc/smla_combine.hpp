@@ -1,93 +1,146 @@
-// Log-sum-exp merge of split results for one token and one group of 16 heads, run by a
-// 256-thread workgroup.  Used by the standalone combine kernel and by the last
+// Log-sum-exp merge of split results for one token and a block of NH heads (16 or 32),
+// run by a 256-thread workgroup.  Used by the standalone combine kernel and by the last
 // workgroup of a token inside the decode kernel.
 //
-// Each split s holds its normalized output O_s[16][512] (fp32, head stride 512) and its
-// natural-log LSE lse_s[16].  lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) O_s.
+// Each split s holds its normalized output O_s[NH][512] (fp32, head stride 512 floats) and
+// its natural-log LSE lse_s[NH].  lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) O_s.
 // A split with lse_s = -inf has weight zero; if every split is -inf the output is zero and
 // lse = -inf.  (The split of the work follows from sizing the decomposition by the token
 // batch: "Prime Intellect Launches Prime Inference, Serving 600B Tokens Daily", section
 // "Four-bit caches make room".)
+//
+// The partials are read through a buffer resource: with kCoherent the loads use the
+// device-coherent policy (partials written by other workgroups of the same launch, through
+// other XCDs' L2), otherwise the default one.  The loads of several splits are issued
+// together, so the merge costs a few memory latencies rather than one per split.
 #pragma once
 
 #include "smla_device.hpp"
 
 namespace smla {
 
-// part(s, &o, &l) yields the fp32 [16][512] output and the [16] LSE of split s.
-// out points at head 0 of the group (head stride out_hstride fp16 elements); lse at head 0.
-// kCoherent: the partials were written by other workgroups of the same launch (read them
-// with device-coherent loads); false when they come from an earlier launch.
-// Thread tid owns head tid/16 and columns 32*(tid%16) .. +31.  The loads of a batch of
-// splits are issued together so that the merge costs a few memory latencies, not one per
-// split.
-template <bool kCoherent, class PartFn>
-__device__ __forceinline__ void lse_merge16(int ns, PartFn part, f16* out, int64_t out_hstride,
-                                            float* lse) {
-  auto ld1 = [](const float* p) { return kCoherent ? load_coherent(p) : *p; };
-  auto ld4 = [](const float* p) { return kCoherent ? load_coherent4(p) : *(const f32x4*)p; };
-  constexpr int kB = 8;   // splits per batch of LSE loads
-  constexpr int kU = 2;   // splits per batch of output loads
+// Buffer resource over [base, base + bytes), raw byte addressing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t merge_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+template <bool kCoherent>
+__device__ __forceinline__ float merge_ld1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherent ? 16 : 0));
+}
+template <bool kCoherent>
+__device__ __forceinline__ f32x4 merge_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent ? 16 : 0));
+}
+
+// part(s, &o_off, &l_off): byte offsets of split s's O[NH][512] within the buffer of `ro`
+// and of its lse[NH] within the buffer of `rl`.  out: head 0 of the block (head stride 512
+// fp16); lse_out: head 0.  scratch: >= 2048 floats of LDS.
+//
+// Phase 1: per-head running maximum and denominator of the LSEs, folded by all threads and
+// reduced through LDS.  Phase 2, per chunk of up to 32 splits: the weights
+// exp(lse_s - lse) go to LDS, then the outputs are summed with every load instruction of a
+// wave reading 1 KB of consecutive bytes (thread tid takes 16-byte pieces tid, tid+256, ...
+// of the NH x 512 block, so one thread covers several heads).
+template <int NH, bool kCoherent, class PartFn>
+__device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
+                                          PartFn part, f16* out, float* lse_out, float* scratch) {
+  static_assert(NH == 16 || NH == 32, "head block");
+  constexpr int K = 256 / NH;          // threads per head in phase 1
+  constexpr int P = NH / 2;            // 16-byte pieces per thread per split (NH*512*4 / 4096)
+  constexpr int U = NH == 16 ? 4 : 2;  // splits per batch of output loads
+  constexpr int CS = 32;               // splits per chunk of weights
   const int tid = threadIdx.x;
-  const int n = tid >> 4;
-  const int c0 = (tid & 15) * 32;
-  float m = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += kB) {
-    float v[kB];
+  float* const red = scratch;                 // [2][256] phase-1 partials
+  float* const mh = scratch + 512;            // [NH] maximum
+  float* const ih = scratch + 512 + NH;       // [NH] 1 / denominator
+  float* const wt = scratch + 1024;           // [CS][NH] weights of a chunk
+
+  // ---- phase 1: thread (h, k) folds splits k, k+K, ...
+  {
+    const int h = tid % NH, k = tid / NH;
+    float m = -INFINITY, d = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += 4 * K) {
+      float v[4];
 #pragma unroll
-    for (int j = 0; j < kB; j++) {
-      const float* o;
-      const float* l;
-      if (s0 + j < ns) {
-        part(s0 + j, &o, &l);
-        v[j] = ld1(l + n);
-      } else {
-        v[j] = -INFINITY;
+      for (int u = 0; u < 4; u++) {
+        const int s = s0 + u * K + k;
+        uint32_t o_off, l_off;
+        part(s < ns ? s : 0, &o_off, &l_off);
+        const float x = merge_ld1<kCoherent>(rl, l_off + 4u * h);
+        v[u] = s < ns ? x : -INFINITY;
       }
-    }
 #pragma unroll
-    for (int j = 0; j < kB; j++) m = fmaxf(m, v[j]);
-  }
-  f32x4 acc[8];
-#pragma unroll
-  for (int k = 0; k < 8; k++) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float den = 0.0f;
-  if (m != -INFINITY) {
-    for (int s0 = 0; s0 < ns; s0 += kU) {
-      float ls[kU];
-      f32x4 ov[kU][8];
-#pragma unroll
-      for (int j = 0; j < kU; j++) {
-        ls[j] = -INFINITY;
-        if (s0 + j < ns) {
-          const float* o;
-          const float* l;
-          part(s0 + j, &o, &l);
-          ls[j] = ld1(l + n);
-          const float* op = o + n * 512 + c0;
-#pragma unroll
-          for (int k = 0; k < 8; k++) ov[j][k] = ld4(op + 4 * k);
+      for (int u = 0; u < 4; u++) {
+        if (v[u] == -INFINITY) continue;
+        if (v[u] > m) {
+          d = d * __expf(m - v[u]) + 1.0f;   // exp(-inf) = 0 on the first value
+          m = v[u];
+        } else {
+          d += __expf(v[u] - m);
         }
       }
+    }
+    red[tid] = m;
+    red[256 + tid] = d;
+  }
+  __syncthreads();
+  if (tid < NH) {
+    float m = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < kU; j++) {
-        if (ls[j] == -INFINITY) continue;   // empty split (or past the end): weight 0
-        const float e = expf(ls[j] - m);
-        den += e;
+    for (int k = 0; k < K; k++) m = fmaxf(m, red[k * NH + tid]);
+    float d = 0.0f;
+    if (m != -INFINITY) {
 #pragma unroll
-        for (int k = 0; k < 8; k++) acc[k] += e * ov[j][k];
+      for (int k = 0; k < K; k++) {
+        const float mk = red[k * NH + tid];
+        if (mk != -INFINITY) d += red[256 + k * NH + tid] * __expf(mk - m);
       }
     }
+    mh[tid] = m;
+    ih[tid] = d > 0.0f ? 1.0f / d : 0.0f;
+    lse_out[tid] = d > 0.0f ? m + logf(d) : -INFINITY;
   }
-  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  f16* dst = out + (int64_t)n * out_hstride + c0;
+  __syncthreads();
+
+  // ---- phase 2: piece q of thread tid holds floats 4*(256q + tid) .. +3 of the block,
+  // i.e. head (256q + tid) / 128, columns 4 * ((256q + tid) % 128) ..
+  f32x4 acc[P];
 #pragma unroll
-  for (int k = 0; k < 8; k += 2) {
-    const f32x4 a = acc[k] * inv, b = acc[k + 1] * inv;
-    *(f16x8*)(dst + 4 * k) = f16x8{(f16)a.x, (f16)a.y, (f16)a.z, (f16)a.w,
-                                   (f16)b.x, (f16)b.y, (f16)b.z, (f16)b.w};
+  for (int q = 0; q < P; q++) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < ns; c0 += CS) {
+    const int cn = min(CS, ns - c0);
+    for (int e = tid; e < cn * NH; e += 256) {
+      const int s = e / NH, h = e - s * NH;
+      uint32_t o_off, l_off;
+      part(c0 + s, &o_off, &l_off);
+      const float ls = merge_ld1<kCoherent>(rl, l_off + 4u * h);
+      wt[e] = (ls == -INFINITY) ? 0.0f : __expf(ls - mh[h]) * ih[h];
+    }
+    __syncthreads();
+    for (int s0 = 0; s0 < cn; s0 += U) {
+      f32x4 ov[U][P];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        uint32_t o_off, l_off;
+        part(c0 + (s0 + u < cn ? s0 + u : 0), &o_off, &l_off);
+#pragma unroll
+        for (int q = 0; q < P; q++) ov[u][q] = merge_ld4<kCoherent>(ro, o_off + 16u * (256 * q + tid));
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        if (s0 + u >= cn) continue;
+#pragma unroll
+        for (int q = 0; q < P; q++) acc[q] += wt[(s0 + u) * NH + (256 * q + tid) / 128] * ov[u][q];
+      }
+    }
+    __syncthreads();
   }
-  if ((tid & 15) == 0) lse[n] = den > 0.0f ? m + logf(den) : -INFINITY;
+#pragma unroll
+  for (int q = 0; q < P; q++) {
+    const int e = 256 * q + tid, h = e / 128, col = 4 * (e % 128);
+    *(f16x4*)(out + 512 * h + col) = f16x4{(f16)acc[q].x, (f16)acc[q].y, (f16)acc[q].z, (f16)acc[q].w};
+  }
 }
 
 }  // namespace smla

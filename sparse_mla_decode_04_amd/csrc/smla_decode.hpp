@@ -2,12 +2,17 @@
 //
 // "Prime Intellect Launches Prime Inference, Serving 600B Tokens Daily", section
 // "Four-bit caches make room": the native kernel sizes its parallel decomposition by the
-// token batch.  Here the T index lists are cut into chunks of kChunkRows entries; the
-// T*ceil(topk/kChunkRows) chunks of every 16-head group form one flat sequence that G
-// workgroups split into equal contiguous ranges (a stream-K split over the index lists).
-// A workgroup whose range covers a token's chunks entirely writes the final output; the
-// workgroups that share a token write normalized partial results, and the last of them
-// to finish merges those partials with a log-sum-exp combine in the same launch.
+// token batch.  Here every token's index list is cut into tiles of kTileRows entries; the
+// T*ceil(topk/kTileRows) tiles form one flat sequence that G workgroups per head block
+// split into equal contiguous ranges (a stream-K split over the index lists).  A range
+// that covers all of a token's tiles writes that token's output directly; a token shared
+// by several ranges gets one normalized partial result from each, and the range that
+// finishes last merges them with a log-sum-exp combine in the same launch.  A range
+// shares at most two tokens with other ranges (its first and its last), so each
+// workgroup owns two partial slots.
+//
+// Heads are processed in blocks of 16*NG: one workgroup gathers and unpacks a row once
+// and applies it to all heads of its block.
 #pragma once
 
 #include <stddef.h>
@@ -15,8 +20,8 @@
 
 namespace smla {
 
-constexpr int kChunkRows = 64;   // list entries per chunk
-constexpr int kHeadGroup = 16;   // heads per workgroup (MFMA N / M dimension)
+constexpr int kTileRows = 64;    // index-list entries per tile
+constexpr int kHeadGroup = 16;   // heads per MFMA tile
 
 struct DecodeArgs {
   const void* q;            // fp16 [T][H][576]
@@ -24,49 +29,61 @@ struct DecodeArgs {
   int64_t pool_rows;
   const int32_t* idx;       // [T][topk]
   int32_t T, H, topk;
-  int32_t cpt;              // chunks per token = ceil(topk / kChunkRows)
-  int64_t chunks;           // T * cpt
-  int32_t G;                // workgroups per head group
-  int32_t max_seg;          // partial slots per workgroup
+  int32_t cpt;              // tiles per token = ceil(topk / kTileRows)
+  int64_t tiles;            // T * cpt
+  int32_t G;                // ranges (workgroups) per head block
+  int32_t HB;               // head blocks = H / (16 * NG)
+  uint32_t rows_bytes;      // bytes addressable through `rows`
+  uint32_t idx_bytes;       // bytes of `idx`
+  uint32_t q_bytes;         // bytes of `q`
   float scale_log2;         // softmax_scale * log2(e)
   void* out;                // fp16 [T][H][512]
   float* lse;               // fp32 [T][H]
-  float* part_o;            // fp32 [HG][G][max_seg][16][512]
-  float* part_lse;          // fp32 [HG][G][max_seg][16]
-  int32_t* counters;        // [HG][T]
+  float* part_o;            // fp32 [HB][G][2][16*NG][512]
+  float* part_lse;          // fp32 [HB][G][2][16*NG]
+  int32_t* counters;        // [HB][T], zero between launches
+  uint32_t part_o_bytes;    // bytes of part_o
+  uint32_t part_lse_bytes;  // bytes of part_lse
 };
 
 struct DecodePlan {
-  int32_t cpt, G, max_seg, HG;
-  int64_t chunks;
+  int32_t cpt, G, HB, NG;
+  int64_t tiles;
   size_t part_o_off, part_lse_off, counters_off, bytes;
 };
 
-// First chunk of workgroup w: floor(w * C / G).
+// First tile of range w: floor(w * C / G).
 __host__ __device__ inline int64_t wg_first_chunk(int64_t w, int64_t C, int64_t G) {
   return w * C / G;
 }
-// The workgroup whose range holds chunk c: the largest w with floor(w*C/G) <= c.
+// The range that holds tile c: the largest w with floor(w*C/G) <= c.
 __host__ __device__ inline int64_t wg_of_chunk(int64_t c, int64_t C, int64_t G) {
   return ((c + 1) * G - 1) / C;
 }
 
+// Head groups per workgroup: two when the head count allows (the unpack of a row is then
+// shared by 32 heads) and a token spans at least two tiles (the two-group kernel stages one
+// query at a time), else one.
+inline int32_t heads_per_block_groups(int32_t H, int32_t topk) {
+  return (H % (2 * kHeadGroup) == 0 && topk > kTileRows) ? 2 : 1;
+}
+
 inline DecodePlan make_plan(int32_t T, int32_t H, int32_t topk, int32_t G) {
   DecodePlan p;
-  p.cpt = (topk + kChunkRows - 1) / kChunkRows;
-  p.chunks = (int64_t)T * p.cpt;
-  p.HG = H / kHeadGroup;
-  if (G > p.chunks) G = (int32_t)p.chunks;
+  p.cpt = (topk + kTileRows - 1) / kTileRows;
+  p.tiles = (int64_t)T * p.cpt;
+  p.NG = heads_per_block_groups(H, topk);
+  p.HB = H / (kHeadGroup * p.NG);
+  if (G > p.tiles) G = (int32_t)p.tiles;
   if (G < 1) G = 1;
   p.G = G;
-  const int64_t per_wg = (p.chunks + G - 1) / G;          // most chunks one workgroup gets
-  p.max_seg = (int32_t)((per_wg + p.cpt - 1) / p.cpt + 1);  // tokens one workgroup can touch
-  const size_t slots = (size_t)p.HG * p.G * p.max_seg;
+  const size_t slots = (size_t)p.HB * p.G * 2;
+  const size_t heads = (size_t)kHeadGroup * p.NG;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.part_o_off = 0;
-  p.part_lse_off = up(slots * kHeadGroup * 512 * sizeof(float));
-  p.counters_off = p.part_lse_off + up(slots * kHeadGroup * sizeof(float));
-  p.bytes = p.counters_off + up((size_t)p.HG * T * sizeof(int32_t));
+  p.part_lse_off = up(slots * heads * 512 * sizeof(float));
+  p.counters_off = p.part_lse_off + up(slots * heads * sizeof(float));
+  p.bytes = p.counters_off + up((size_t)p.HB * T * sizeof(int32_t));
   return p;
 }
 
