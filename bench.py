@@ -102,6 +102,19 @@ def cpu_baseline(wl, q, idx, src, seconds):
                       f"BLAS with {blas} threads"}
 
 
+def copy_calibration(nbytes=256 << 20, reps=5):
+    """A copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch of this copy,
+    against its 256 MiB read and 256 MiB written, give the factors that turn those counters
+    into HBM bytes."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +124,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget, 0 disables")
     ap.add_argument("--check-tokens", type=int, default=3, help="tokens checked against the oracle (untimed)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -127,6 +142,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     smla.lib()
     dev = "cuda"
     wl = W.WORKLOADS[args.config]

@@ -32,6 +32,11 @@
  *   - Index lists: int32, -1 (any negative value) marks an empty entry.  An entry
  *     >= pool_rows is treated as empty as well, so no list entry can make a kernel read
  *     outside the pool.
+ *   - Size limit: the decode and combine kernels address each array through a buffer
+ *     resource with a 32-bit byte range, so each of the query, the index lists, the
+ *     cache pool (pool_rows * 352 bytes; about 12.2 million rows), the staged FP8 rows,
+ *     the partial results and the workspace must stay below 0xFFFFFFE0 bytes.  A call
+ *     beyond that returns SMLA_ERR_UNSUPPORTED.
  */
 #ifndef SMLA_H
 #define SMLA_H
@@ -98,8 +103,11 @@ SMLA_API int nvfp4_unpack_rows_f16(const void* kv_pool_dev, int64_t pool_rows, c
  *   lse_dev      fp32 [T][H]:       ln sum_j exp(softmax_scale * q.k_j)
  * An entry list with no valid entry gives out = 0 and lse = -inf.  Repeated rows count
  * once per entry.  H must be a multiple of 16; 1 <= topk <= 65536.
- *   num_splits   0 = automatic.  Otherwise the number of workgroups per 16-head group
- *                that share the T*ceil(topk/64) row chunks (clamped to that count).
+ * Heads are processed in blocks: 32 heads per workgroup when H is a multiple of 32 and
+ * topk > 64 (one unpack of a row then serves 32 heads), else 16.
+ *   num_splits   0 = automatic (smla_choose_num_splits).  Otherwise the number of
+ *                workgroups per head block that share the T*ceil(topk/64) tiles of 64
+ *                list entries, in equal contiguous ranges (clamped to [1, tile count]).
  *   workspace    device scratch of at least smla_decode_workspace_bytes(T, H, topk,
  *                num_splits) bytes, zero-filled before its first use.  Every call
  *                leaves the counters it uses at zero again, so a workspace can be
@@ -113,10 +121,21 @@ SMLA_API int sparse_mla_decode(const void* q_dev, const void* kv_pool_dev, int64
                       float softmax_scale, void* out_dev, float* lse_dev, int32_t num_splits,
                       void* workspace_dev, size_t workspace_bytes, void* stream);
 
-/* The split count the automatic mode of sparse_mla_decode uses for this shape. */
+/*
+ * The split count the automatic mode of sparse_mla_decode uses for this shape on the
+ * current device: with fewer (token, head block) pairs than compute units, every token
+ * is cut into the same number of tile-aligned ranges so that about one workgroup runs
+ * per compute unit; otherwise the workgroups that fit the device at once share the tiles
+ * (at least two tiles each).  Queries the current device's compute-unit count.
+ * Returns 0 for T == 0 or a shape sparse_mla_decode rejects.
+ */
 SMLA_API int32_t smla_choose_num_splits(int32_t T, int32_t H, int32_t topk);
 
-/* Workspace bytes sparse_mla_decode needs (num_splits as passed to it, 0 = automatic). */
+/*
+ * Workspace bytes sparse_mla_decode needs (num_splits as passed to it, 0 = automatic).
+ * Also an upper bound for sparse_mla_decode_fp8rows with the same arguments, whose
+ * automatic split count is never larger.
+ */
 SMLA_API size_t smla_decode_workspace_bytes(int32_t T, int32_t H, int32_t topk, int32_t num_splits);
 
 /*

@@ -35,14 +35,28 @@ int cu_count() {
   return cus;
 }
 
+// Workgroups per head block.  Few (token, head block) pairs: every token gets the same
+// number of ranges, aligned to its tiles (so each range writes at most one partial and a
+// token's merge reads few of them), one workgroup per CU.  Otherwise the stream-K ranges
+// fill every resident workgroup slot once.
 int32_t auto_splits(bool fp8rows, int32_t T, int32_t H, int32_t topk) {
   const int64_t cpt = (topk + kTileRows - 1) / kTileRows;
   const int64_t C = (int64_t)T * cpt;
   const int NG = heads_per_block_groups(H, topk);
-  const int HB = H / (kHeadGroup * NG);
-  int64_t G = (int64_t)cu_count() * decode_wgs_per_cu(fp8rows, NG) / (HB > 0 ? HB : 1);
-  const int64_t cap = C / kMinTilesPerWg;
-  if (G > cap) G = cap;
+  const int64_t HB = H / (kHeadGroup * NG);
+  const int64_t cus = cu_count();
+  int64_t G;
+  if ((int64_t)T * HB < cus) {
+    int64_t S = cus / ((int64_t)T * HB);
+    const int64_t smax = cpt / kMinTilesPerWg;
+    if (S > smax) S = smax;
+    if (S < 1) S = 1;
+    G = (int64_t)T * S;
+  } else {
+    G = cus * decode_wgs_per_cu(fp8rows, NG) / HB;
+    const int64_t cap = C / kMinTilesPerWg;
+    if (G > cap) G = cap;
+  }
   if (G < 1) G = 1;
   if (G > C) G = C;
   return (int32_t)G;
