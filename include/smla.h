@@ -35,8 +35,9 @@
  *   - Size limit: the decode and combine kernels address each array through a buffer
  *     resource with a 32-bit byte range, so each of the query, the index lists, the
  *     cache pool (pool_rows * 352 bytes; about 12.2 million rows), the staged FP8 rows,
- *     the partial results and the workspace must stay below 0xFFFFFFE0 bytes.  A call
- *     beyond that returns SMLA_ERR_UNSUPPORTED.
+ *     the partial results and the workspace must stay within 0xFFFFF000 bytes, and a
+ *     decode call must have fewer than 2^31 tiles of 64 list entries (T * ceil(topk/64)).
+ *     A call beyond that returns SMLA_ERR_UNSUPPORTED.
  */
 #ifndef SMLA_H
 #define SMLA_H

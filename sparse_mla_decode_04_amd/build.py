@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsmla.so")
-SOURCES = ["codec.hip", "decode.hip", "api.hip"]
+SOURCES = ["codec.hip", "decode.hip", "decode_regs.hip", "api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -2,6 +2,8 @@
 // layout and kernel launches.  Declarations and contracts: include/smla.h.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <atomic>
 
@@ -15,7 +17,18 @@ using namespace smla;
 
 constexpr int kMinTilesPerWg = 2;     // below this the partial results outweigh the rows
 constexpr int kMaxTopk = 65536;
-constexpr uint64_t kMaxBufferBytes = 0xFFFFFFE0ull;   // byte range of one buffer resource
+constexpr uint64_t kMaxBufferBytes = 0xFFFFF000ull;   // byte range of one buffer resource (kOOB)
+
+// Decode kernel for 16-head blocks, read once from SMLA_DECODE_VARIANT: "ring" (LDS-ring
+// gather) or "regs" (register gather, PV overlapped with QK^T; the default).  Other
+// head-block sizes always use the LDS-ring kernel.
+int decode_variant() {
+  static const int v = [] {
+    const char* e = getenv("SMLA_DECODE_VARIANT");
+    return (e != nullptr && strcmp(e, "ring") == 0) ? 0 : 1;
+  }();
+  return v;
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -90,6 +103,7 @@ int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
   const uint64_t rows_bytes = fp8rows ? (uint64_t)T * topk * 576 : (uint64_t)pool_rows * 352;
   if (idx_bytes > kMaxBufferBytes || rows_bytes > kMaxBufferBytes || q_bytes > kMaxBufferBytes)
     return SMLA_ERR_UNSUPPORTED;
+  if ((int64_t)T * ((topk + kTileRows - 1) / kTileRows) >= (int64_t)1 << 31) return SMLA_ERR_UNSUPPORTED;
   const int32_t G = num_splits > 0 ? num_splits : auto_splits(fp8rows, T, H, topk);
   const DecodePlan p = make_plan(T, H, topk, G);
   if (p.bytes > kMaxBufferBytes) return SMLA_ERR_UNSUPPORTED;
@@ -118,7 +132,7 @@ int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
   a.part_o_bytes = (uint32_t)(p.part_lse_off - p.part_o_off);
   a.part_lse_bytes = (uint32_t)(p.counters_off - p.part_lse_off);
   const hipError_t e = fp8rows ? launch_decode_fp8rows(a, (hipStream_t)stream)
-                               : launch_decode_nvfp4(a, (hipStream_t)stream);
+                               : launch_decode_nvfp4(a, (hipStream_t)stream, decode_variant());
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 

@@ -58,24 +58,12 @@
 // The same skeleton with kFp8 = true is pass 2 of the staged variant: it attends over
 // 576-byte FP8 E4M3 rows written to HBM by pass 1 (one per list entry), reading V^T
 // through the 8-bit LDS transpose read.
-#include "smla_combine.hpp"
-#include "smla_device.hpp"
 #include "smla_launch.hpp"
-
-// The LDS DMA sequences below set m0 themselves and declare it clobbered.
-#pragma clang diagnostic ignored "-Winline-asm"
+#include "smla_tile.hpp"
 
 namespace smla {
 
 namespace {
-
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWaves = 4;
-constexpr int kWR = 16;                 // rows per wave per tile
-constexpr int kPH = 72;                 // fp16 stride of the [.][tile row] tables
-constexpr float kSlack = 8.0f;          // log2 units
-constexpr uint32_t kOOB = 0xFFFFFFE0u;  // buffer offset beyond every range: reads as zero
 
 template <bool kFp8>
 struct RowFmt {
@@ -84,16 +72,6 @@ struct RowFmt {
   static constexpr int kLoads = (kPieces + 3) / 4;           // DMA per wave per tile: 9 or 6
   static constexpr int kPortion = kPieces * 256;             // LDS bytes of one wave's rows
   static constexpr int kSlot = kWaves * kPortion;            // LDS bytes of one tile
-};
-
-// Query staging: the 16*NG query rows of a token (1152 bytes each) as 16-byte pieces with
-// one spare piece per row (row stride 1168 bytes keeps the register loads conflict-free),
-// filled by kLoads DMA instructions of 1 KB.
-template <int NG>
-struct QFmt {
-  static constexpr int kSlots = kHeadGroup * NG * 73;        // 72 pieces + 1 spare per head
-  static constexpr int kLoads = (kSlots + 63) / 64;          // 19 or 37
-  static constexpr int kBytes = kLoads * 1024;
 };
 
 // Staging buffers for the query: one suffices unless the distance is two tiles and a
@@ -114,110 +92,9 @@ struct __attribute__((aligned(16))) Smem {
   int flag;
 };
 
-// Buffer resource over [base, base + bytes): raw byte addressing; an offset at or past
-// `bytes` reads as zero without a memory access.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = (uint64_t)base;
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));
-  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-  r.w = 0x00020000;   // 32-bit data format, no swizzle
-  return r;
-}
-
-// LDS DMA: lane l's 16 (4) bytes at buffer offset voff land at LDS byte lds + 16*l (4*l).
-// Issued as inline assembly so the compiler neither waits for nor reorders around them
-// implicitly; every consumer waits with an explicit vmcnt.
-__device__ __forceinline__ void dma16(i32x4 rs, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rs)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(i32x4 rs, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rs)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N): vector memory operations complete in issue order, so this waits
-// for everything but the N most recent.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// LDS byte address of p (wave-uniform: DMA destinations go through m0).
-__device__ __forceinline__ uint32_t lds_addr(const SMLA_LDS void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-
 __device__ __forceinline__ u32x2 lds_read_tr8(const SMLA_LDS void* p) {
   i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SMLA_LDS i32x2*)p);
   return u32x2{(uint32_t)v.x, (uint32_t)v.y};
-}
-
-// Sum of eight fp16 values in fp32.
-__device__ __forceinline__ float sum8(f16x8 v) {
-  const f16x2 one = f16x2{(f16)1.0f, (f16)1.0f};
-  float s = __builtin_amdgcn_fdot2(f16x2{v[0], v[1]}, one, 0.0f, false);
-  s = __builtin_amdgcn_fdot2(f16x2{v[2], v[3]}, one, s, false);
-  s = __builtin_amdgcn_fdot2(f16x2{v[4], v[5]}, one, s, false);
-  return __builtin_amdgcn_fdot2(f16x2{v[6], v[7]}, one, s, false);
-}
-
-// Tile cursor: flat tile c -> token t and tile ci within the token, advanced one at a time.
-struct Cursor {
-  int64_t c;
-  int64_t t;
-  int32_t ci;
-  __device__ void init(int64_t c0, int32_t cpt) {
-    c = c0;
-    t = c0 / cpt;
-    ci = (int32_t)(c0 - t * cpt);
-  }
-  __device__ void next(int32_t cpt) {
-    c++;
-    if (++ci == cpt) {
-      ci = 0;
-      t++;
-    }
-  }
-};
-
-template <int NG>
-struct QReg {
-  f16x8 v[NG][18];   // B operand of QK step k: features 128g+8k.. (k < 16), 512+16g+8(k-16)..
-};
-
-// Query registers of token t for lane (head r16, group g): heads head0 + 16j + r16.
-template <int NG>
-__device__ __forceinline__ void load_q(const DecodeArgs& A, int64_t t, int head0, int r16, int g,
-                                       QReg<NG>& Q) {
-#pragma unroll
-  for (int j = 0; j < NG; j++) {
-    const f16* base = (const f16*)A.q + ((t * A.H + head0 + kHeadGroup * j + r16) * kHeadDim);
-#pragma unroll
-    for (int k = 0; k < 16; k++) Q.v[j][k] = *(const f16x8*)(base + 128 * g + 8 * k);
-    Q.v[j][16] = *(const f16x8*)(base + kLatent + 16 * g);
-    Q.v[j][17] = *(const f16x8*)(base + kLatent + 16 * g + 8);
-  }
-}
-
-// Query registers from the staging area (layout of QFmt).
-template <int NG>
-__device__ __forceinline__ void read_q(const SMLA_LDS uint8_t* qs, int r16, int g, QReg<NG>& Q) {
-#pragma unroll
-  for (int j = 0; j < NG; j++) {
-    const SMLA_LDS uint8_t* h = qs + (kHeadGroup * j + r16) * 1168;
-#pragma unroll
-    for (int k = 0; k < 16; k++) Q.v[j][k] = lds_load<f16x8>(h + 16 * (16 * g + k));
-    Q.v[j][16] = lds_load<f16x8>(h + 16 * (64 + 2 * g));
-    Q.v[j][17] = lds_load<f16x8>(h + 16 * (65 + 2 * g));
-  }
 }
 
 }  // namespace
@@ -250,6 +127,8 @@ __global__ __launch_bounds__(256, WPC) void sparse_mla_decode_kernel(DecodeArgs 
   const i32x4 rs_rows = make_rsrc(A.rows, A.rows_bytes);
   const i32x4 rs_idx = make_rsrc(A.idx, A.idx_bytes);
   const i32x4 rs_q = make_rsrc(A.q, A.q_bytes);
+  const __amdgpu_buffer_rsrc_t ws_o = merge_rsrc(A.part_o, A.part_o_bytes);
+  const __amdgpu_buffer_rsrc_t ws_l = merge_rsrc(A.part_lse, A.part_lse_bytes);
   SMLA_LDS uint8_t* const ring = (SMLA_LDS uint8_t*)sm.ring;
   SMLA_LDS int32_t* const idxbuf = (SMLA_LDS int32_t*)sm.idx;
 
@@ -257,18 +136,12 @@ __global__ __launch_bounds__(256, WPC) void sparse_mla_decode_kernel(DecodeArgs 
   auto issue_idx = [&](const Cursor& cur, int i) {
     const int k = cur.ci * kTileRows + kWR * wid + lane;
     const bool ok = cur.c < c_hi && k < A.topk;
-    const uint32_t voff = ok ? (uint32_t)((cur.t * A.topk + k) * 4) : kOOB;
+    const uint32_t voff = ok ? (uint32_t)(cur.t * A.topk + k) * 4u : kOOB;
     if (lane < kWR) dma4(rs_idx, voff, lds_addr(idxbuf + ((i & 1) * kWaves + wid) * kWR));
   };
-  // DMA of this wave's share (instructions wid, wid+4, ...) of the query rows of token t.
+  // DMA of this wave's share of the query rows of token t into its staging buffer.
   auto issue_q = [&](int64_t t) {
-    const uint32_t lds0 = lds_addr((SMLA_LDS uint8_t*)sm.qst[t % QB]);
-    for (int kk = wid; kk < QFmt<NG>::kLoads; kk += kWaves) {
-      const int sl = 64 * kk + lane, h = sl / 73, p = sl - 73 * h;
-      const bool ok = h < NH && p < 72;
-      const uint32_t voff = ok ? (uint32_t)((t * A.H + head0 + h) * (int64_t)(2 * kHeadDim)) + 16u * p : kOOB;
-      dma16(rs_q, voff, lds0 + 1024u * kk);
-    }
+    dma_q<NG>(A, rs_q, t, head0, wid, lane, lds_addr((SMLA_LDS uint8_t*)sm.qst[t % QB]));
   };
   // DMA of this wave's rows of tile cur into ring slot i % ST (its index entries must have
   // landed), preceded by the query of its token when the tile starts a token (i >= 1).
@@ -282,7 +155,7 @@ __global__ __launch_bounds__(256, WPC) void sparse_mla_decode_kernel(DecodeArgs 
     const bool ok = cur.c < c_hi && k < A.topk && row_valid(v, A.pool_rows);
     uint32_t base;
     if constexpr (kFp8)
-      base = (uint32_t)((cur.t * A.topk + k) * (int64_t)kHeadDim);
+      base = (uint32_t)(cur.t * A.topk + k) * (uint32_t)kHeadDim;
     else
       base = (uint32_t)v * (uint32_t)kRowBytes;
     const uint32_t lds0 = lds_addr(ring + (i % ST) * F::kSlot + wid * F::kPortion);
@@ -542,32 +415,8 @@ __global__ __launch_bounds__(256, WPC) void sparse_mla_decode_kernel(DecodeArgs 
       const int64_t tok0 = t * cpt;
       const bool full = (c_lo <= tok0) && (c_hi >= tok0 + cpt);
       const int seg = (t == t_first) ? 0 : 1;
-      const int64_t slot_id = ((int64_t)hb * G + w) * 2 + seg;
-#pragma unroll
-      for (int j = 0; j < NG; j++) {
-        const float Ls = wave_sum_xor16_32(l_acc[j]);
-        const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-        const float lse_nat = Ls > 0.0f ? (m_ref[j] + log2f(Ls)) * kLn2 : -INFINITY;
-        const int hl = kHeadGroup * j + r16;   // head within the block
-        if (full) {
-          f16* op = (f16*)A.out + (t * A.H + head0 + hl) * kLatent;
-#pragma unroll
-          for (int k = 0; k < 8; k++) {
-            const f32x4 v = O[j][k] * inv;
-            *(f16x4*)(op + 16 * (8 * wid + k) + 4 * g) = f16x4{(f16)v.x, (f16)v.y, (f16)v.z, (f16)v.w};
-          }
-          if (wid == 0 && g == 0) A.lse[t * A.H + head0 + hl] = lse_nat;
-        } else {
-          float* po = A.part_o + (slot_id * NH + hl) * kLatent;
-#pragma unroll
-          for (int k = 0; k < 8; k++) store_coherent(po + 16 * (8 * wid + k) + 4 * g, O[j][k] * inv);
-          if (wid == 0 && g == 0) store_coherent(A.part_lse + slot_id * NH + hl, lse_nat);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; k++) O[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_ref[j] = -INFINITY;
-        l_acc[j] = 0.0f;
-      }
+      finish_segment<NG>(A, O, m_ref, l_acc, t, full, ((int64_t)hb * G + w) * 2 + seg, head0, wid, g, r16,
+                         ws_o, ws_l);
       if (!full) pend_t[seg] = t;
     }
     cu.next(cpt);
@@ -575,44 +424,9 @@ __global__ __launch_bounds__(256, WPC) void sparse_mla_decode_kernel(DecodeArgs 
     for (int d = 0; d < D; d++) vmq[d] = vmq[d + 1];
   }
 
-  // ---- publish this range's partials (all stores complete), and merge the tokens whose
-  // last range this is
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const __amdgpu_buffer_rsrc_t ws_o = merge_rsrc(A.part_o, A.part_o_bytes);
-  const __amdgpu_buffer_rsrc_t ws_l = merge_rsrc(A.part_lse, A.part_lse_bytes);
-  float* const scratch = (float*)sm.ring;   // the ring is idle from here on
-#pragma unroll
-  for (int seg = 0; seg < 2; seg++) {
-    const int64_t t = pend_t[seg];
-    if (t < 0) continue;
-    const int64_t tok0 = t * cpt;
-    const int64_t w_lo = wg_of_chunk(tok0, C, G), w_hi = wg_of_chunk(tok0 + cpt - 1, C, G);
-    if (tid == 0) {
-      int32_t* cnt = A.counters + (int64_t)hb * A.T + t;
-      const int old = atomicAdd(cnt, 1);
-      const int last = (old == (int)(w_hi - w_lo));
-      if (last) atomicExch(cnt, 0);
-      sm.flag = last;
-    }
-    __syncthreads();
-    const int last = sm.flag;
-    __syncthreads();
-    if (!last) continue;
-    // split s of token t is range w_lo + s.  Every range after w_lo starts inside the
-    // token, so t is its first token (slot 0); range w_lo holds t in slot 1 exactly when
-    // it starts before the token.
-    const uint32_t sl0 = (uint32_t)(((int64_t)hb * G + w_lo) * 2);
-    const uint32_t seg0 = (wg_first_chunk(w_lo, C, G) < tok0) ? 1u : 0u;
-    auto part = [&](int s, uint32_t* o_off, uint32_t* l_off) {
-      const uint32_t sl = sl0 + 2u * (uint32_t)s + (s == 0 ? seg0 : 0u);
-      *o_off = sl * (uint32_t)(NH * kLatent * 4);
-      *l_off = sl * (uint32_t)(NH * 4);
-    };
-    lse_merge<NH, true>((int)(w_hi - w_lo + 1), ws_o, ws_l, part,
-                        (f16*)A.out + (t * A.H + head0) * kLatent, A.lse + t * A.H + head0, scratch);
-    __syncthreads();
-  }
+  // ---- publish this range's partials and merge the tokens whose last range this is (the
+  // ring is idle from here on and serves as the merge's scratch)
+  publish_and_merge<NH>(A, pend_t, hb, head0, ws_o, ws_l, &sm.flag, (float*)sm.ring);
 }
 
 __global__ __launch_bounds__(256) void sparse_mla_combine_kernel(const float* __restrict__ part_o,
@@ -643,9 +457,10 @@ hipError_t launch_variant(const DecodeArgs& a, hipStream_t s) {
 
 int decode_wgs_per_cu(bool fp8rows, int32_t NG) { return (!fp8rows && NG == 1) ? 2 : 1; }
 
-hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s) {
-  return (a.HB * 2 * kHeadGroup == a.H) ? launch_variant<2, 3, false, 1>(a, s)
-                                        : launch_variant<1, 2, false, 2>(a, s);
+hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s, int variant) {
+  if (a.HB * 2 * kHeadGroup == a.H) return launch_variant<2, 3, false, 1>(a, s);
+  if (variant == 1) return launch_decode_nvfp4_regs(a, s);
+  return launch_variant<1, 2, false, 2>(a, s);
 }
 
 hipError_t launch_decode_fp8rows(const DecodeArgs& a, hipStream_t s) {

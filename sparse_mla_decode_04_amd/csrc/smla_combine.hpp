@@ -33,6 +33,19 @@ __device__ __forceinline__ f32x4 merge_ld4(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent ? 16 : 0));
 }
 
+// The eight XCDs of MI355X each have a private L2.  Partial results that one workgroup hands
+// to another inside a launch are written with the device-coherent policy (sc1: written
+// through the private L2 to memory) and read with it (read around the private L2); the
+// hand-off is ordered by waiting for the stores to complete before the counter update, so
+// no L2 write-back or invalidate is needed.  One 16-byte store per piece: split into smaller
+// stores, each piece would cost several partial-line writes.
+__device__ __forceinline__ void merge_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 16);
+}
+__device__ __forceinline__ void merge_st1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 16);
+}
+
 // part(s, &o_off, &l_off): byte offsets of split s's O[NH][512] within the buffer of `ro`
 // and of its lse[NH] within the buffer of `rl`.  out: head 0 of the block (head stride 512
 // fp16); lse_out: head 0.  scratch: >= 2048 floats of LDS.
@@ -42,10 +55,63 @@ __device__ __forceinline__ f32x4 merge_ld4(__amdgpu_buffer_rsrc_t r, uint32_t of
 // exp(lse_s - lse) go to LDS, then the outputs are summed with every load instruction of a
 // wave reading 1 KB of consecutive bytes (thread tid takes 16-byte pieces tid, tid+256, ...
 // of the NH x 512 block, so one thread covers several heads).
+//
+// Few splits (ns <= SMAX): every thread loads the LSEs of its own heads and its output
+// pieces of every split at once -- one memory round trip -- and computes the weights of
+// its heads itself.
+template <int NH, int SMAX, bool kCoherent, class PartFn>
+__device__ __forceinline__ void lse_merge_few(int ns, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
+                                              PartFn part, f16* out, float* lse_out) {
+  constexpr int P = NH / 2;   // 16-byte pieces per thread: piece q is head (256q + tid) / 128
+  const int tid = threadIdx.x;
+  const int h1 = tid >> 7;    // head of piece q is 2q + h1
+  float ls[SMAX][P];
+  f32x4 ov[SMAX][P];
+#pragma unroll
+  for (int s = 0; s < SMAX; s++) {
+    uint32_t o_off, l_off;
+    part(s < ns ? s : 0, &o_off, &l_off);
+#pragma unroll
+    for (int q = 0; q < P; q++) {
+      ls[s][q] = merge_ld1<kCoherent>(rl, l_off + 4u * (2 * q + h1));
+      ov[s][q] = merge_ld4<kCoherent>(ro, o_off + 16u * (256 * q + tid));
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < P; q++) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < SMAX; s++)
+      if (s < ns) m = fmaxf(m, ls[s][q]);
+    float d = 0.0f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < SMAX; s++) {
+        if (s < ns && ls[s][q] != -INFINITY) {
+          const float wgt = __expf(ls[s][q] - m);
+          d += wgt;
+          acc += wgt * ov[s][q];
+        }
+      }
+    }
+    const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+    const int e = 256 * q + tid, h = e / 128, col = 4 * (e % 128);
+    const f32x4 v = acc * inv;
+    *(f16x4*)(out + 512 * h + col) = f16x4{(f16)v.x, (f16)v.y, (f16)v.z, (f16)v.w};
+    if ((e % 128) == 0) lse_out[h] = d > 0.0f ? m + logf(d) : -INFINITY;
+  }
+}
+
 template <int NH, bool kCoherent, class PartFn>
 __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
                                           PartFn part, f16* out, float* lse_out, float* scratch) {
   static_assert(NH == 16 || NH == 32, "head block");
+  constexpr int kFew = NH == 16 ? 4 : 2;
+  if (ns <= kFew) {
+    lse_merge_few<NH, kFew, kCoherent>(ns, ro, rl, part, out, lse_out);
+    return;
+  }
   constexpr int K = 256 / NH;          // threads per head in phase 1
   constexpr int P = NH / 2;            // 16-byte pieces per thread per split (NH*512*4 / 4096)
   constexpr int U = NH == 16 ? 4 : 2;  // splits per batch of output loads

@@ -141,40 +141,22 @@ __device__ __forceinline__ void lds_store(void* p, T v) {
   *(SMLA_LDS T*)p = v;
 }
 
-// ------------------------------------------------------------------ cross-XCD data --
-// The eight XCDs of MI355X each have a private L2.  Results that one workgroup hands to
-// another inside a launch are written and read as relaxed device-scope atomics, which
-// gfx950 performs write-through / read-around the private L2 (the "sc1" policy); the
-// hand-off is then ordered by waiting for the stores to complete before the counter
-// update, without writing back or invalidating the whole L2.
-__device__ __forceinline__ void store_coherent(float* p, f32x4 v) {
-  u32x4 u = __builtin_bit_cast(u32x4, v);
-  __hip_atomic_store((uint64_t*)p, (uint64_t)u.x | ((uint64_t)u.y << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store((uint64_t*)p + 1, (uint64_t)u.z | ((uint64_t)u.w << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ f32x4 load_coherent4(const float* p) {
-  const uint64_t a = __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load((uint64_t*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __builtin_bit_cast(f32x4, u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)});
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load((float*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
+// Reductions over the four lanes l, l^16, l^32, l^48 with the gfx950 lane-swap
+// instructions (no LDS round trip).  permlane16_swap(v, v) yields, in every lane, the
+// values of its even and its odd 16-lane row; permlane32_swap(v, v) those of its lower and
+// upper 32-lane half.  Every lane of a quadruple combines the same operands in the same
+// order, so all four get bit-identical results.
 __device__ __forceinline__ float wave_max_xor16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_sum_xor16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 }  // namespace smla
