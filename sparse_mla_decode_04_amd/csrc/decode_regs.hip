@@ -137,6 +137,44 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
     for (int kk = 0; kk < 4; kk++) lds_store<u32x4>(cp + 256 * (4 * g + kk), R.cw[kk]);
   };
 
+  // ---- the same, refilling R with the next tile's row (lane base vb) piece by piece as
+  // QK^T finishes with each piece, so the row loads of a wave trickle into the memory
+  // pipeline between its matrix steps instead of queueing behind the other waves' loads.
+  // The fences order each piece's last use (its MFMAs, whose results feed acc, and its
+  // LDS store) before its reload, so every piece keeps one set of registers.
+  auto qk_refill = [&](RowRegs& R, int par, const QReg<1>& Q, f32x4 (&acc)[2], uint32_t vb) {
+    f16x2 s01 = e4m3x2<false>(R.sc.x), s23 = e4m3x2<true>(R.sc.x);
+    f16x2 s45 = e4m3x2<false>(R.sc.y), s67 = e4m3x2<true>(R.sc.y);
+    asm volatile("" : "+v"(s01), "+v"(s23), "+v"(s45), "+v"(s67) : : "memory");
+    R.sc = ld64(rs_rows, vb + lane_s);
+    const f16 sf[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
+    SMLA_LDS uint8_t* const cp = codes + par * kCodeSlot + wid * kCodePortion + 16 * r16;
+#pragma unroll
+    for (int kq = 0; kq < 4; kq++) {
+#pragma unroll
+      for (int k = 4 * kq; k < 4 * kq + 4; k++) {
+        const f16 sk = sf[k >> 1];
+        acc[k & 1] = mfma16x16x32(unpack8(R.cw[kq][k & 3], f16x2{sk, sk}), Q.v[0][k], acc[k & 1]);
+      }
+      lds_store<u32x4>(cp + 256 * (4 * g + kq), R.cw[kq]);
+      asm volatile("" : "+v"(acc[0]), "+v"(acc[1]) : : "memory");
+      R.cw[kq] = ld128(rs_rows, vb + lane_c + 16u * kq);
+    }
+    acc[0] = mfma16x16x32(fp8x8(R.rope.x, R.rope.y), Q.v[0][16], acc[0]);
+    acc[1] = mfma16x16x32(fp8x8(R.rope.z, R.rope.w), Q.v[0][17], acc[1]);
+    asm volatile("" : "+v"(acc[0]), "+v"(acc[1]) : : "memory");
+    R.rope = ld128(rs_rows, vb + lane_r);
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) sm.sc[par][8 * g + jj][row] = sf[jj];   // zero for an empty row
+  };
+  // Lane base of row v for tile cur (out of range if the entry is empty) and the wave's
+  // valid-row mask.
+  auto row_base = [&](const Cursor& cur, int32_t v, uint32_t& vmask) -> uint32_t {
+    const bool ok = cur.c < c_hi && cur.ci * kTileRows + row < A.topk && row_valid(v, A.pool_rows);
+    vmask = __builtin_amdgcn_readfirstlane((uint32_t)__ballot(ok && g == 0) & 0xFFFFu);
+    return ok ? __umul24((uint32_t)v, (uint32_t)kRowBytes) : kOOB;
+  };
+
   f32x4 O[1][8];
   float m_ref[1] = {-INFINITY}, l_acc[1] = {0.0f};
 #pragma unroll
@@ -259,8 +297,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
 
   // ---- prologue: query of the first token; index entries of tiles 0 and 1; rows of
   // tile 0.  The loop then issues per tile i: [query DMA], rows(i+1), idx(i+2).
-  // The query loads go last: waiting for the first index entries then does not wait for
-  // them, and they travel together with the rows of tile 0.
+  // The query comes once per workgroup by LDS DMA, issued after the rows of tile 0 (so the
+  // wait for the first index entries does not cover it) and read into every wave's
+  // registers from LDS: a quarter of the memory traffic of four waves loading it each.
   Cursor cr, cx;   // next row load (tile i+1) and index load (tile i+2)
   cr.init(c_lo, cpt);
   cx.init(c_lo, cpt);
@@ -271,8 +310,11 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   RowRegs RR;
   uint32_t vm = issue_rows(cr, v0, RR);
   cr.next(cpt);
+  dma_q<1>(A, rs_q, c_lo / cpt, head0, wid, lane, qst_lds);
+  wait_vm<0>();
+  __syncthreads();
   QReg<1> Q;
-  load_q<1>(A, c_lo / cpt, head0, r16, g, Q);
+  read_q<1>((const SMLA_LDS uint8_t*)sm.qst, r16, g, Q);
 
   // The fence after each QK^T ties the refill of RR to the end of QK^T (its results and
   // LDS writes come first), so the old and new contents of RR never overlap and share
@@ -305,18 +347,17 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
     const int par = i & 1, ppar = par ^ 1;
     const bool new_seg = cu.ci == cpt - 1;   // tile i starts a later token
     if (new_seg) new_token_q(cu.t + 1, Q);
+    stage_q(i);
     f16x8 bop[2];
     const int fl = pv_operand(ppar, bop);
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    qk(RR, par, Q, acc);
     const uint32_t vmi = vm;
-    asm volatile("" : "+v"(acc[0]), "+v"(acc[1]) : : "memory");
-    rescale(ppar, fl, bop);
-    stage_q(i);
-    vm = issue_rows(cr, IV, RR);
+    const uint32_t vb = row_base(cr, IV, vm);   // rows of tile i+1
     cr.next(cpt);
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    qk_refill(RR, par, Q, acc, vb);
     IV = issue_idx(cx);
     cx.next(cpt);
+    rescale(ppar, fl, bop);
     softmax(acc, vmi, par, new_seg ? -INFINITY : m_ref[0]);
     pv(ppar, bop);
     segment_end(i - 1);
