@@ -6,6 +6,7 @@ load the in-tree build.
 """
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -38,11 +39,23 @@ def _hipcc():
 
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, "-Rpass-analysis=kernel-resource-usage", *extra, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    return obj, r.stderr
+    # A kernel that spills registers to scratch memory runs several times slower: refuse it.
+    kernel, remarks = None, []
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            kernel = m.group(1)
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            raise RuntimeError(f"{src}: kernel {kernel} spills to scratch ({m.group(1)} bytes/lane)")
+        if "remark:" not in line and not re.match(r"^\s*(\d+\s*)?\|", line) and line.strip() != "^":
+            remarks.append(line)
+    return obj, "\n".join(remarks)
 
 
 def build(verbose=False, extra=()):
