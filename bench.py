@@ -22,6 +22,7 @@ oracle on the host on the same workload.
 """
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -39,9 +40,8 @@ MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16 matrix, published
 ROW_BYTES = 352
 COLD_SPAN_BYTES = 2 << 30      # layer copies span at least this much
 METRIC = "sparse NVFP4 MLA decode: µs/launch, tokens/s, achieved HBM GB/s vs peak"
-KERNEL_SOURCES = ["sparse_mla_decode_04_amd/csrc/decode.hip", "sparse_mla_decode_04_amd/csrc/smla_device.hpp",
-                  "sparse_mla_decode_04_amd/csrc/smla_combine.hpp", "sparse_mla_decode_04_amd/csrc/smla_decode.hpp",
-                  "sparse_mla_decode_04_amd/csrc/api.hip"]
+KERNEL_SOURCES = sorted(os.path.relpath(p, ROOT) for p in
+                        glob.glob(os.path.join(ROOT, "sparse_mla_decode_04_amd", "csrc", "*.[hc]*")))
 
 
 def log(*a):
