@@ -16,7 +16,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsmla.so")
-SOURCES = ["codec.hip", "decode.hip", "decode_regs.hip", "api.hip"]
+SOURCES = ["codec.hip", "decode.hip", "decode_regs.hip", "decode_h64.hip", "api.hip"]
+# per-source flags: the 64-head kernel keeps its 128-value accumulator in the MFMA
+# accumulation registers, so it is built without the VGPR-only MFMA form
+NO_VGPR_FORM = {"decode_h64.hip"}
 ARCH = "gfx950"
 
 FLAGS = [
@@ -39,7 +42,8 @@ def _hipcc():
 
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *FLAGS, "-Rpass-analysis=kernel-resource-usage", *extra, "-c",
+    flags = [f for f in FLAGS if src not in NO_VGPR_FORM or f not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
+    cmd = [_hipcc(), *flags, "-Rpass-analysis=kernel-resource-usage", *extra, "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

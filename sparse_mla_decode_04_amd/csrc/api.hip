@@ -55,7 +55,7 @@ int cu_count() {
 int32_t auto_splits(bool fp8rows, int32_t T, int32_t H, int32_t topk) {
   const int64_t cpt = (topk + kTileRows - 1) / kTileRows;
   const int64_t C = (int64_t)T * cpt;
-  const int NG = heads_per_block_groups(H, topk);
+  const int NG = heads_per_block_groups(H, topk, fp8rows);
   const int64_t HB = H / (kHeadGroup * NG);
   const int64_t cus = cu_count();
   int64_t G;
@@ -105,7 +105,7 @@ int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
     return SMLA_ERR_UNSUPPORTED;
   if ((int64_t)T * ((topk + kTileRows - 1) / kTileRows) >= (int64_t)1 << 31) return SMLA_ERR_UNSUPPORTED;
   const int32_t G = num_splits > 0 ? num_splits : auto_splits(fp8rows, T, H, topk);
-  const DecodePlan p = make_plan(T, H, topk, G);
+  const DecodePlan p = make_plan(T, H, topk, G, fp8rows);
   if (p.bytes > kMaxBufferBytes) return SMLA_ERR_UNSUPPORTED;
   if (p.bytes > 0 && (ws == nullptr || ws_bytes < p.bytes || !aligned16(ws))) return SMLA_ERR_WORKSPACE;
   DecodeArgs a;
@@ -180,7 +180,9 @@ SMLA_API int32_t smla_choose_num_splits(int32_t T, int32_t H, int32_t topk) {
 SMLA_API size_t smla_decode_workspace_bytes(int32_t T, int32_t H, int32_t topk, int32_t num_splits) {
   if (!decode_shape_ok(T, H, topk) || H % kHeadGroup != 0 || T == 0 || num_splits < 0) return 0;
   const int32_t G = num_splits > 0 ? num_splits : auto_splits(false, T, H, topk);
-  return make_plan(T, H, topk, G).bytes;
+  const int32_t G8 = num_splits > 0 ? num_splits : auto_splits(true, T, H, topk);
+  const size_t b4 = make_plan(T, H, topk, G, false).bytes, b8 = make_plan(T, H, topk, G8, true).bytes;
+  return b4 > b8 ? b4 : b8;   // enough for either entry point
 }
 
 SMLA_API int sparse_mla_decode(const void* q, const void* pool, int64_t pool_rows, const int32_t* idx,

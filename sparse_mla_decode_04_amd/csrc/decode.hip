@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256) void sparse_mla_combine_kernel(const float* __
     *l_off = base * 4u;
   };
   lse_merge<kHeadGroup, false>(S, ro, rl, part, out + ((int64_t)t * H + kHeadGroup * hg) * kLatent,
-                               lse + (int64_t)t * H + kHeadGroup * hg, scratch);
+                               lse + (int64_t)t * H + kHeadGroup * hg, scratch, (int)threadIdx.x);
 }
 
 namespace {
@@ -458,6 +458,7 @@ hipError_t launch_variant(const DecodeArgs& a, hipStream_t s) {
 int decode_wgs_per_cu(bool fp8rows, int32_t NG) { return (!fp8rows && NG == 1) ? 2 : 1; }
 
 hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s, int variant) {
+  if (a.HB * 4 * kHeadGroup == a.H) return launch_decode_nvfp4_h64(a, s);
   if (a.HB * 2 * kHeadGroup == a.H) return launch_variant<2, 3, false, 1>(a, s);
   if (variant == 1) return launch_decode_nvfp4_regs(a, s);
   return launch_variant<1, 2, false, 2>(a, s);

@@ -1,5 +1,6 @@
 // Log-sum-exp merge of split results for one token and a block of NH heads (16 or 32),
-// run by a 256-thread workgroup.  Used by the standalone combine kernel and by the last
+// run by a team of 256 threads (a whole workgroup, or one half of a 512-thread one; `tid`
+// is the thread's index in the team).  Used by the standalone combine kernel and by the last
 // workgroup of a token inside the decode kernel.
 //
 // Each split s holds its normalized output O_s[NH][512] (fp32, head stride 512 floats) and
@@ -61,9 +62,8 @@ __device__ __forceinline__ void merge_st1(__amdgpu_buffer_rsrc_t r, uint32_t off
 // its heads itself.
 template <int NH, int SMAX, bool kCoherent, class PartFn>
 __device__ __forceinline__ void lse_merge_few(int ns, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
-                                              PartFn part, f16* out, float* lse_out) {
+                                              PartFn part, f16* out, float* lse_out, int tid) {
   constexpr int P = NH / 2;   // 16-byte pieces per thread: piece q is head (256q + tid) / 128
-  const int tid = threadIdx.x;
   const int h1 = tid >> 7;    // head of piece q is 2q + h1
   float ls[SMAX][P];
   f32x4 ov[SMAX][P];
@@ -105,18 +105,17 @@ __device__ __forceinline__ void lse_merge_few(int ns, __amdgpu_buffer_rsrc_t ro,
 
 template <int NH, bool kCoherent, class PartFn>
 __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
-                                          PartFn part, f16* out, float* lse_out, float* scratch) {
+                                          PartFn part, f16* out, float* lse_out, float* scratch, int tid) {
   static_assert(NH == 16 || NH == 32, "head block");
   constexpr int kFew = NH == 16 ? 4 : 2;
   if (ns <= kFew) {
-    lse_merge_few<NH, kFew, kCoherent>(ns, ro, rl, part, out, lse_out);
+    lse_merge_few<NH, kFew, kCoherent>(ns, ro, rl, part, out, lse_out, tid);
     return;
   }
   constexpr int K = 256 / NH;          // threads per head in phase 1
   constexpr int P = NH / 2;            // 16-byte pieces per thread per split (NH*512*4 / 4096)
   constexpr int U = NH == 16 ? 4 : 2;  // splits per batch of output loads
   constexpr int CS = 32;               // splits per chunk of weights
-  const int tid = threadIdx.x;
   float* const red = scratch;                 // [2][256] phase-1 partials
   float* const mh = scratch + 512;            // [NH] maximum
   float* const ih = scratch + 512 + NH;       // [NH] 1 / denominator

@@ -61,18 +61,21 @@ __host__ __device__ inline int64_t wg_of_chunk(int64_t c, int64_t C, int64_t G) 
   return ((c + 1) * G - 1) / C;
 }
 
-// Head groups per workgroup: two when the head count allows (the unpack of a row is then
-// shared by 32 heads) and a token spans at least two tiles (the two-group kernel stages one
-// query at a time), else one.
-inline int32_t heads_per_block_groups(int32_t H, int32_t topk) {
-  return (H % (2 * kHeadGroup) == 0 && topk > kTileRows) ? 2 : 1;
+// Head groups of 16 per workgroup.  The unpack of a row is shared by all heads of a block,
+// so blocks are as large as the head count allows: 64 heads (NVFP4 rows only), else 32,
+// else 16.  Blocks of 32 or 64 need a token to span at least two tiles (those kernels
+// stage one query at a time).
+inline int32_t heads_per_block_groups(int32_t H, int32_t topk, bool fp8rows) {
+  if (topk <= kTileRows) return 1;
+  if (!fp8rows && H % (4 * kHeadGroup) == 0) return 4;
+  return H % (2 * kHeadGroup) == 0 ? 2 : 1;
 }
 
-inline DecodePlan make_plan(int32_t T, int32_t H, int32_t topk, int32_t G) {
+inline DecodePlan make_plan(int32_t T, int32_t H, int32_t topk, int32_t G, bool fp8rows) {
   DecodePlan p;
   p.cpt = (topk + kTileRows - 1) / kTileRows;
   p.tiles = (int64_t)T * p.cpt;
-  p.NG = heads_per_block_groups(H, topk);
+  p.NG = heads_per_block_groups(H, topk, fp8rows);
   p.HB = H / (kHeadGroup * p.NG);
   if (G > p.tiles) G = (int32_t)p.tiles;
   if (G < 1) G = 1;

@@ -238,7 +238,7 @@ __device__ __forceinline__ void publish_and_merge(const DecodeArgs& A, const int
       *l_off = sl * (uint32_t)(NH * 4);
     };
     lse_merge<NH, true>((int)(w_hi - w_lo + 1), ws_o, ws_l, part,
-                        (f16*)A.out + (t * A.H + head0) * kLatent, A.lse + t * A.H + head0, scratch);
+                        (f16*)A.out + (t * A.H + head0) * kLatent, A.lse + t * A.H + head0, scratch, tid);
     __syncthreads();
   }
 }

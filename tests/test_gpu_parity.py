@@ -145,6 +145,8 @@ SMALL = [  # T, H, N, K, empty_frac, seed
     (3, 16, 900, 65, 0.5, 6),       # one full chunk plus one entry
     (2, 16, 100, 1, 0.0, 7),        # a single entry
     (6, 128, 3000, 256, 0.2, 8),
+    (5, 64, 4000, 700, 0.1, 9),     # 64-head blocks, ragged last chunk
+    (3, 192, 3000, 1000, 0.3, 10),  # three 64-head blocks
 ]
 
 
@@ -168,8 +170,20 @@ def test_decode_every_split_count(smla, splits):
     assert_parity(out, lse, ref_out, ref_lse, f"splits {splits}")
 
 
-def test_all_empty_tokens_and_split_segments(smla):
-    wl, src, q, idx = _setup(6, 16, 3000, 512, 0.0, 12)
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 1000])
+def test_decode_every_split_count_64_heads(smla, splits):
+    _say("splits 64 heads", splits)
+    wl, src, q, idx = _setup(5, 64, 6000, 900, 0.1, 18)
+    pool = build_device_pool(src, DEV)
+    out, lse = _run_decode(smla, q, pool, idx, wl.softmax_scale, num_splits=splits)
+    ref_out, ref_lse = oracle.sparse_mla_decode_ref(q, OracleRows(src), idx, wl.softmax_scale)
+    assert_parity(out, lse, ref_out, ref_lse, f"64 heads splits {splits}")
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_all_empty_tokens_and_split_segments(smla, H):
+    _say("empties", H)
+    wl, src, q, idx = _setup(6, H, 3000, 512, 0.0, 12)
     idx[1, :] = -1                       # whole list empty
     idx[3, 100:] = -1                    # later chunks of a list empty
     idx[4, :300] = -1                    # early chunks empty
@@ -184,8 +198,10 @@ def test_all_empty_tokens_and_split_segments(smla):
         assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
 
 
-def test_identical_rows_give_the_latent_bit_exact(smla):
-    wl, src, q, _ = _setup(2, 16, 64, 64, 0.0, 13)
+@pytest.mark.parametrize("H", [16, 64])
+def test_identical_rows_give_the_latent_bit_exact(smla, H):
+    _say("identical rows", H)
+    wl, src, q, _ = _setup(2, H, 64, 64, 0.0, 13)
     pool = build_device_pool(src, DEV)
     idx = np.full((2, 2048), -1, dtype=np.int32)
     idx[0, :1500] = 17
