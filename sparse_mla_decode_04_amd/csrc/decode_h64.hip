@@ -166,19 +166,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
         const int par = s & 1;
         const SMLA_LDS uint8_t* const slot = ring + (s % kST) * kSlot;
         const int ln = fresh_lane(lane), r16 = ln & 15, g = ln >> 4;
-        if (s > 0) {
-          // shared references after tile s-1: the larger one the row halves used
-          const int pp = par ^ 1;
-          const int fl = sm.wflag[pp][0] | sm.wflag[pp][1] | sm.wflag[pp][2] | sm.wflag[pp][3];
-          if (fl & 1) {
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-              const int h = 32 * hh + 16 * j + r16;
-              mq[j] = fmaxf(sm.wref[pp][0][h], sm.wref[pp][1][h]);
-            }
-          }
-        }
-        if (cu.ci == 0) {
+        const bool new_seg = cu.ci == 0;
+        if (new_seg) {
           // the first tile of a token starts a new segment; a later token's query is
           // loaded here (with it every DMA issued so far completes)
           mq[0] = mq[1] = -INFINITY;
@@ -187,11 +176,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
             wait_vm<0>();
           }
         }
-        // rows of tile s+2, index entries of tile s+4
-        issue_rows(cr, s + 2, ln);
-        cr.next(cpt);
-        issue_idx(cx, s + 4, ln);
-        cx.next(cpt);
 
         // ---- QK^T: rows 32rh + 16m + r16 (m = 0, 1) against heads 32hh + 16j + r16
         const uint32_t vrow = sm.vmask[s % kST][2 * rh] | (sm.vmask[s % kST][2 * rh + 1] << 16);
@@ -245,16 +229,34 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
 #pragma unroll
             for (int q = 0; q < 4; q++) sp[m][q] = f16x2{(f16)0.0f, (f16)0.0f};
         }
-        // PV scale table: the head-half-0 waves write their rows' scales (empty rows: 0)
+        // PV scale table: the head-half-0 waves write their rows' scales (an empty row was
+        // fetched as zeros, so its scales are 0)
         if (hh == 0) {
 #pragma unroll
           for (int m = 0; m < 2; m++) {
-            const bool rv = (vrow >> (16 * m + r16)) & 1;
             const int row = 32 * rh + 16 * m + r16;
 #pragma unroll
-            for (int jj = 0; jj < 8; jj++) {
-              const f16 v = (jj & 1) ? sp[m][jj >> 1].y : sp[m][jj >> 1].x;
-              sm.sc[par][8 * g + jj][row] = rv ? v : (f16)0.0f;
+            for (int jj = 0; jj < 8; jj++)
+              sm.sc[par][8 * g + jj][row] = (jj & 1) ? sp[m][jj >> 1].y : sp[m][jj >> 1].x;
+          }
+        }
+
+        // ---- rows of tile s+2, index entries of tile s+4 (issued behind the matrix work)
+        issue_rows(cr, s + 2, ln);
+        cr.next(cpt);
+        issue_idx(cx, s + 4, ln);
+        cx.next(cpt);
+
+        // ---- shared references after tile s-1 of the same segment: the larger one the row
+        // halves used
+        if (s > 0 && !new_seg) {
+          const int pp = par ^ 1;
+          const int fl = sm.wflag[pp][0] | sm.wflag[pp][1] | sm.wflag[pp][2] | sm.wflag[pp][3];
+          if (fl & 1) {
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+              const int h = 32 * hh + 16 * j + r16;
+              mq[j] = fmaxf(sm.wref[pp][0][h], sm.wref[pp][1][h]);
             }
           }
         }
