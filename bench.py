@@ -22,7 +22,6 @@ oracle on the host on the same workload.
 """
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -40,17 +39,32 @@ MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16 matrix, published
 ROW_BYTES = 352
 COLD_SPAN_BYTES = 2 << 30      # layer copies span at least this much
 METRIC = "sparse NVFP4 MLA decode: µs/launch, tokens/s, achieved HBM GB/s vs peak"
-KERNEL_SOURCES = sorted(os.path.relpath(p, ROOT) for p in
-                        glob.glob(os.path.join(ROOT, "sparse_mla_decode_04_amd", "csrc", "*.[hc]*")))
+CSRC = os.path.join("sparse_mla_decode_04_amd", "csrc")
+# A decode kernel's sources: its own file, the shared device headers and the host code that
+# sizes its launch.  A counter summary stays valid while these are unchanged.
+SHARED_SOURCES = ["api.hip", "smla_combine.hpp", "smla_decode.hpp", "smla_device.hpp", "smla_launch.hpp",
+                  "smla_tile.hpp"]
+KERNEL_FILES = {"sparse_mla_decode_regs_kernel": "decode_regs.hip",
+                "sparse_mla_decode_h64_kernel": "decode_h64.hip",
+                "sparse_mla_decode_kernel": "decode.hip"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
+def kernel_sources(kernel):
+    """Source files of the decode kernel whose (possibly demangled) name contains one of
+    KERNEL_FILES' keys."""
+    own = [f for k, f in KERNEL_FILES.items() if k + "(" in kernel or kernel.endswith(k)]
+    if len(own) != 1:
+        raise ValueError(f"unknown decode kernel {kernel!r}")
+    return [os.path.join(CSRC, f) for f in own + SHARED_SOURCES]
+
+
+def kernel_hash(kernel):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in kernel_sources(kernel):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -66,7 +80,10 @@ def traffic_from_profiles(workload):
         d = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if d.get("kernel_hash") != kernel_hash():
+    try:
+        if d.get("kernel_hash") != kernel_hash(d.get("kernel", "")):
+            return None
+    except ValueError:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -102,6 +119,41 @@ def cpu_baseline(wl, q, idx, src, seconds):
                       f"BLAS with {blas} threads"}
 
 
+def staged_timing(binding, wl, layers, q_d, idx_d, out, lse, ws, fused_ms, steps):
+    """The staged two-pass variant the pages compare against: pass 1 writes every listed
+    row as FP8 E4M3 to a [T][topk][576] buffer in HBM, pass 2 attends over it.  Timed with
+    events around each pass on the launch stream, over the same layer copies."""
+    import torch
+    staged = torch.empty((wl.T, wl.topk, 576), dtype=torch.uint8, device="cuda")
+    L = len(layers)
+
+    def run(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        binding.nvfp4_stage_fp8(layers[i % L], idx_d, staged)
+        if ev is not None:
+            ev[1].record()
+        binding.sparse_mla_decode_fp8rows(q_d, staged, idx_d, wl.pool_rows, wl.softmax_scale, out, lse, 0, ws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(2):
+        run(i)
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for i in range(steps):
+        run(2 + i, evs[i])
+    torch.cuda.synchronize()
+    p1 = float(np.mean([a.elapsed_time(b) for a, b, c in evs])) * 1e3
+    p2 = float(np.mean([b.elapsed_time(c) for a, b, c in evs])) * 1e3
+    log(f"staged variant: pass 1 (unpack to FP8 in HBM) {p1:.1f} us, pass 2 (attend) {p2:.1f} us, "
+        f"total {p1 + p2:.1f} us vs fused {fused_ms * 1e3:.1f} us")
+    del staged
+    torch.cuda.empty_cache()
+    return {"stage_us": p1, "attend_us": p2, "us_per_launch": p1 + p2, "fused_us": fused_ms * 1e3,
+            "fused_speedup": (p1 + p2) / (fused_ms * 1e3), "steps": steps}
+
+
 def copy_calibration(nbytes=256 << 20, reps=5):
     """A copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch of this copy,
     against its 256 MiB read and 256 MiB written, give the factors that turn those counters
@@ -124,6 +176,9 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget, 0 disables")
     ap.add_argument("--check-tokens", type=int, default=3, help="tokens checked against the oracle (untimed)")
+    ap.add_argument("--staged", type=int, default=-1,
+                    help="also time the staged two-pass variant for this many steps "
+                         "(default: 20 for the cache-write workload, else 0)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -183,6 +238,8 @@ def main():
     def step(i, ev=None):
         l = i % L
         if pack:
+            if ev is not None:
+                ev[2].record()
             pack[l]()
         if ev is not None:
             ev[0].record()
@@ -206,7 +263,7 @@ def main():
             print("bench.py: output does not match the oracle", file=sys.stderr)
             sys.exit(3)
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -214,12 +271,18 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kms = np.array([a.elapsed_time(b) for a, b in evs])
+    kms = np.array([a.elapsed_time(b) for a, b, _ in evs])
     k_avg = float(np.mean(kms))
     achieved = kv_bytes / (k_avg * 1e-3) / 1e9
     log(f"decode launch: mean {k_avg * 1e3:.2f} us, median {np.median(kms) * 1e3:.2f} us, "
         f"min {np.min(kms) * 1e3:.2f} us; step {ms_per_step * 1e3:.2f} us; "
         f"gathered KV {kv_bytes / 1e6:.2f} MB -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    pack_us = float(np.mean([c.elapsed_time(a) for a, b, c in evs])) * 1e3 if pack else None
+    if pack:
+        log(f"cache write ({len(slots)} rows): mean {pack_us:.2f} us")
+    staged_steps = args.staged if args.staged >= 0 else (20 if pack else 0)
+    staged = staged_timing(binding, wl, layers, q_d, idx_d, out, lse, ws, k_avg, staged_steps) if staged_steps else None
 
     traffic = traffic_from_profiles(wl.name)
     flops = 2.0 * wl.H * (576 + 512) * n_valid        # QK^T over 576 + PV over 512, per valid entry
@@ -251,6 +314,10 @@ def main():
                    "us_per_launch": k_avg * 1e3},
         "roofline": roof,
     }
+    if pack:
+        res["config"]["cache_write_us"] = pack_us
+    if staged:
+        res["staged_variant"] = staged
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(wl, q, idx, src_full, args.cpu_seconds)
         log(f"cpu oracle: {res['cpu_baseline']['value']:.1f} tokens/s")

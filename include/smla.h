@@ -104,8 +104,9 @@ SMLA_API int nvfp4_unpack_rows_f16(const void* kv_pool_dev, int64_t pool_rows, c
  *   lse_dev      fp32 [T][H]:       ln sum_j exp(softmax_scale * q.k_j)
  * An entry list with no valid entry gives out = 0 and lse = -inf.  Repeated rows count
  * once per entry.  H must be a multiple of 16; 1 <= topk <= 65536.
- * Heads are processed in blocks: 32 heads per workgroup when H is a multiple of 32 and
- * topk > 64 (one unpack of a row then serves 32 heads), else 16.
+ * Heads are processed in blocks per workgroup: 64 heads when H is a multiple of 64 and
+ * topk > 64, else 32 when H is a multiple of 32 and topk > 64, else 16.  A larger block
+ * lets one unpack of a row serve more heads.
  *   num_splits   0 = automatic (smla_choose_num_splits).  Otherwise the number of
  *                workgroups per head block that share the T*ceil(topk/64) tiles of 64
  *                list entries, in equal contiguous ranges (clamped to [1, tile count]).
@@ -164,7 +165,8 @@ SMLA_API int nvfp4_stage_fp8(const void* kv_pool_dev, int64_t pool_rows, const i
  * Staged variant, pass 2: attention over the FP8 rows written by nvfp4_stage_fp8
  * (E4M3 -> fp16 exactly, FP16 operands, FP32 accumulation).  indices_dev only marks
  * which entries are empty.  Arguments otherwise as in sparse_mla_decode, with
- * smla_decode_workspace_bytes giving the workspace size.
+ * smla_decode_workspace_bytes giving the workspace size; heads are processed in blocks of
+ * 32 or 16 (never 64).
  */
 SMLA_API int sparse_mla_decode_fp8rows(const void* q_dev, const void* staged_dev,
                               const int32_t* indices_dev, int64_t pool_rows, int32_t T, int32_t H,
