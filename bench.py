@@ -45,7 +45,7 @@ CSRC = os.path.join("sparse_mla_decode_04_amd", "csrc")
 SHARED_SOURCES = ["api.hip", "smla_combine.hpp", "smla_decode.hpp", "smla_device.hpp", "smla_launch.hpp",
                   "smla_tile.hpp"]
 KERNEL_FILES = {"sparse_mla_decode_regs_kernel": "decode_regs.hip",
-                "sparse_mla_decode_h64_kernel": "decode_h64.hip",
+                "sparse_mla_decode_ws_kernel": "decode_ws.hip",
                 "sparse_mla_decode_kernel": "decode.hip"}
 
 
@@ -56,7 +56,8 @@ def log(*a):
 def kernel_sources(kernel):
     """Source files of the decode kernel whose (possibly demangled) name contains one of
     KERNEL_FILES' keys."""
-    own = [f for k, f in KERNEL_FILES.items() if k + "(" in kernel or kernel.endswith(k)]
+    own = [f for k, f in KERNEL_FILES.items()
+           if k + "(" in kernel or k + "<" in kernel or kernel.endswith(k)]
     if len(own) != 1:
         raise ValueError(f"unknown decode kernel {kernel!r}")
     return [os.path.join(CSRC, f) for f in own + SHARED_SOURCES]

@@ -20,12 +20,14 @@ constexpr int kMaxTopk = 65536;
 constexpr uint64_t kMaxBufferBytes = 0xFFFFF000ull;   // byte range of one buffer resource (kOOB)
 
 // Decode kernel for 16-head blocks, read once from SMLA_DECODE_VARIANT: "ring" (LDS-ring
-// gather) or "regs" (register gather, PV overlapped with QK^T; the default).  Other
-// head-block sizes always use the LDS-ring kernel.
+// gather), "ws" (scoring and accumulating waves) or "regs" (register gather, PV overlapped
+// with QK^T; the default).  Other head-block sizes have one kernel each.
 int decode_variant() {
   static const int v = [] {
     const char* e = getenv("SMLA_DECODE_VARIANT");
-    return (e != nullptr && strcmp(e, "ring") == 0) ? 0 : 1;
+    if (e != nullptr && strcmp(e, "ring") == 0) return 0;
+    if (e != nullptr && strcmp(e, "ws") == 0) return 2;
+    return 1;
   }();
   return v;
 }
@@ -66,7 +68,7 @@ int32_t auto_splits(bool fp8rows, int32_t T, int32_t H, int32_t topk) {
     if (S < 1) S = 1;
     G = (int64_t)T * S;
   } else {
-    G = cus * decode_wgs_per_cu(fp8rows, NG) / HB;
+    G = cus * decode_wgs_per_cu(fp8rows, NG, decode_variant()) / HB;
     const int64_t cap = C / kMinTilesPerWg;
     if (G > cap) G = cap;
   }

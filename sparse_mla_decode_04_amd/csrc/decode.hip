@@ -455,12 +455,15 @@ hipError_t launch_variant(const DecodeArgs& a, hipStream_t s) {
 }
 }  // namespace
 
-int decode_wgs_per_cu(bool fp8rows, int32_t NG) { return (!fp8rows && NG == 1) ? 2 : 1; }
+int decode_wgs_per_cu(bool fp8rows, int32_t NG, int variant) {
+  return (!fp8rows && NG == 1 && variant != 2) ? 2 : 1;
+}
 
 hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s, int variant) {
-  if (a.HB * 4 * kHeadGroup == a.H) return launch_decode_nvfp4_h64(a, s);
+  if (a.HB * 4 * kHeadGroup == a.H) return launch_decode_nvfp4_ws(a, s, 64);
   if (a.HB * 2 * kHeadGroup == a.H) return launch_variant<2, 3, false, 1>(a, s);
   if (variant == 1) return launch_decode_nvfp4_regs(a, s);
+  if (variant == 2) return launch_decode_nvfp4_ws(a, s, 16);
   return launch_variant<1, 2, false, 2>(a, s);
 }
 

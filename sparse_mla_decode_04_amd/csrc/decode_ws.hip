@@ -1,4 +1,6 @@
-// Fused sparse MLA decode over NVFP4 cache rows for blocks of 64 heads (gfx950 / MI355X).
+// Fused sparse MLA decode over NVFP4 cache rows with waves specialised by role: scoring
+// waves and accumulating waves (gfx950 / MI355X).  One kernel template for head blocks of
+// 64 (the default at 64 and more heads) and of 16.
 //
 // "Prime Intellect Launches Prime Inference, Serving 600B Tokens Daily", section
 // "Four-bit caches make room": per decode token, only the cache rows named by the sparse
@@ -7,11 +9,8 @@
 // kernel overlaps unpacking with scoring and accumulation by giving the stages to
 // different warp groups; this kernel does the same with two roles of four waves each.
 //
-// With 64 or more heads the matrix work per gathered byte is above the machine balance,
-// so the kernel is organised to keep the matrix cores fed: one workgroup of eight waves
-// per CU applies each row to 64 heads, every unpacked operand feeds several MFMAs, and
-// each SIMD runs one scoring wave and one accumulating wave, which issue into its VALU and
-// matrix core in turn.
+// One workgroup of eight waves per CU; each SIMD runs one scoring wave and one
+// accumulating wave, which issue into its VALU and matrix core in turn.
 //
 //  * Step s (one barrier per step): the scoring waves score tile s while the accumulating
 //    waves apply the probabilities of tile s-1 to its rows.
@@ -19,17 +18,19 @@
 //    four slots (tile s-1 being accumulated, tile s being scored, two in flight); scoring
 //    wave w fetches rows 16w..16w+15 of a tile, piece-major; empty entries read as zeros
 //    without a memory access; index entries run two tiles ahead of the rows.
-//  * QK^T (scoring wave (r, hh) = (w & 1, w >> 1)): rows 32r..32r+31 against heads
-//    32hh..32hh+31; per K step it unpacks two row fragments (A operands) and issues four
-//    MFMAs against the two head fragments of its query registers.
-//  * Softmax per head over the tile's 64 rows, shared between the two row halves through a
-//    per-head reference in LDS (a row half keeps the shared reference unless its rows
+//  * QK^T: the scoring waves cover the tile's 64 rows x NH heads as RG row groups x HW head
+//    groups; scoring wave w takes row group w % RG (MT tiles of 16 rows) and head group
+//    w / RG (JT tiles of 16 heads).  Per K step it unpacks MT row fragments (A operands)
+//    and issues MT*JT MFMAs against its JT query fragments.  NH = 64: 32 rows x 32 heads
+//    per wave (each row unpacked by two waves); NH = 16: 16 rows x 16 heads.
+//  * Softmax per head over the tile's 64 rows, shared between the row groups through a
+//    per-head reference in LDS (a row group keeps the shared reference unless its rows
 //    exceed it by more than the slack); probabilities and the rows' group scales to LDS.
-//  * PV (accumulating wave p): output features 128p..128p+127 for all 64 heads,
+//  * PV (accumulating wave p): output features 128p..128p+127 for all NH heads,
 //    O^T += V^T P^T; each unpacked V^T fragment (4-bit transpose read of the ring, times
-//    the group scales) feeds four MFMAs, one per 16 heads.
+//    the group scales) feeds NH/16 pairs of MFMAs.
 //  * Split epilogue as in the other kernels; the in-launch merge runs as two teams of four
-//    waves, 32 heads each.
+//    waves (NH = 64: 32 heads each; NH = 16: the first team, the second joins its barriers).
 #include "smla_launch.hpp"
 #include "smla_tile.hpp"
 
@@ -37,7 +38,6 @@ namespace smla {
 
 namespace {
 
-constexpr int kH = 64;                    // heads per workgroup
 constexpr int kPieces = kRowBytes / 16;   // 22
 constexpr int kLoads = 6;                 // DMA instructions per scoring wave per tile (pieces 0..23)
 constexpr int kPortion = kPieces * 256;   // one scoring wave's 16 rows, [piece][row]
@@ -45,17 +45,27 @@ constexpr int kSlot = kWaves * kPortion;  // one tile
 constexpr int kST = 4;                    // ring slots
 constexpr int kThreads = 2 * kWaves * 64; // scoring waves 0..3, accumulating waves 4..7
 
-struct __attribute__((aligned(16))) Smem64 {
-  uint8_t ring[kST][kSlot];          // [slot][portion][piece][row] 16-byte pieces
-  int32_t idx[2][kWaves][kWR];       // index-list DMA landing zone [tile parity][portion]
-  f16 sc[2][32][kPH];                // PV scales [parity][group][tile row]
-  f16 pb[2][kH][kPH];                // probabilities [parity][head][tile row]
-  float wref[2][2][kH];              // reference each row half used [parity][half][head]
-  int wflag[2][kWaves];              // bit 0: wave raised a reference; bit 1: wave has a row
-  uint32_t vmask[kST][kWaves];       // valid rows of each DMA portion [slot][portion]
+template <int NH>
+struct WsShape {
+  static_assert(NH == 16 || NH == 64, "head block");
+  static constexpr int JT = NH == 64 ? 2 : 1;   // 16-head tiles per scoring wave
+  static constexpr int HW = NH / (16 * JT);     // head groups of scoring waves
+  static constexpr int RG = kWaves / HW;        // row groups of scoring waves
+  static constexpr int MT = 4 / RG;             // 16-row tiles per scoring wave
+  static constexpr int NJ = NH / 16;            // 16-head tiles of an accumulating wave
+};
+
+template <int NH>
+struct __attribute__((aligned(16))) SmemWs {
+  uint8_t ring[kST][kSlot];               // [slot][portion][piece][row] 16-byte pieces
+  int32_t idx[2][kWaves][kWR];            // index-list DMA landing zone [tile parity][portion]
+  f16 sc[2][32][kPH];                     // PV scales [parity][group][tile row]
+  f16 pb[2][NH][kPH];                     // probabilities [parity][head][tile row]
+  float wref[2][WsShape<NH>::RG][NH];     // reference each row group used [parity][group][head]
+  int wflag[2][kWaves];                   // bit 0: wave raised a reference; bit 1: wave has a row
+  uint32_t vmask[kST][kWaves];            // valid rows of each DMA portion [slot][portion]
   int flag;
 };
-static_assert(sizeof(Smem64) <= 160 * 1024, "LDS of one CU");
 
 // The lane id behind an empty volatile asm: per-lane addresses derived from it inside the
 // tile loop are recomputed each tile instead of being hoisted into registers that stay live
@@ -67,8 +77,12 @@ __device__ __forceinline__ int fresh_lane(int lane) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(DecodeArgs A) {
-  __shared__ Smem64 sm;
+template <int NH>
+__global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(DecodeArgs A) {
+  using S = WsShape<NH>;
+  constexpr int JT = S::JT, RG = S::RG, MT = S::MT, NJ = S::NJ;
+  static_assert(sizeof(SmemWs<NH>) <= 160 * 1024, "LDS of one CU");
+  __shared__ SmemWs<NH> sm;
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -82,14 +96,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
   const int cpt = A.cpt;
   const int64_t c_lo = wg_first_chunk(w, C, G), c_hi = wg_first_chunk(w + 1, C, G);
   const int n = (int)(c_hi - c_lo);
-  const int head0 = hb * kH;
+  const int head0 = hb * NH;
   SMLA_LDS uint8_t* const ring = (SMLA_LDS uint8_t*)sm.ring;
   const __amdgpu_buffer_rsrc_t ws_o = merge_rsrc(A.part_o, A.part_o_bytes);
   const __amdgpu_buffer_rsrc_t ws_l = merge_rsrc(A.part_lse, A.part_lse_bytes);
 
   if (wid < kWaves) {
     // =============================== scoring waves ===============================
-    const int rh = wid & 1, hh = wid >> 1;   // row half, head half
+    const int rg = wid % RG, hg = wid / RG;   // row group, head group
     const float sl2 = A.scale_log2;
     const i32x4 rs_rows = make_rsrc(A.rows, A.rows_bytes);
     const i32x4 rs_idx = make_rsrc(A.idx, A.idx_bytes);
@@ -122,14 +136,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
       if (ln == 0) sm.vmask[i % kST][wid] = vm;
     };
 
-    // Query registers of the wave's 32 heads: Q[j][k] = B operand of QK step k for head
-    // 32hh + 16j + r16 (latent features 128g + 8k.., rope 512 + 16g + 8(k-16)..).
-    f16x8 Q[2][18];
-    auto load_q2 = [&](int64_t t, int ln) {
+    // Query registers of the wave's 16*JT heads: Q[j][k] = B operand of QK step k for head
+    // 16*JT*hg + 16j + r16 (latent features 128g + 8k.., rope 512 + 16g + 8(k-16)..).
+    f16x8 Q[JT][18];
+    auto load_q = [&](int64_t t, int ln) {
       const int r16 = ln & 15, g = ln >> 4;
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const f16* base = (const f16*)A.q + ((t * A.H + head0 + 32 * hh + 16 * j + r16) * kHeadDim);
+      for (int j = 0; j < JT; j++) {
+        const f16* base = (const f16*)A.q + ((t * A.H + head0 + 16 * JT * hg + 16 * j + r16) * kHeadDim);
 #pragma unroll
         for (int k = 0; k < 16; k++) Q[j][k] = *(const f16x8*)(base + 128 * g + 8 * k);
         Q[j][16] = *(const f16x8*)(base + kLatent + 16 * g);
@@ -144,7 +158,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
     cr.init(c_lo, cpt);
     cx.init(c_lo, cpt);
     cu.init(c_lo, cpt);
-    load_q2(cu.t, lane);
+    load_q(cu.t, lane);
     issue_idx(cx, 0, lane);
     cx.next(cpt);
     issue_idx(cx, 1, lane);
@@ -160,7 +174,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
     wait_vm<kLoads + 1>();   // rows(0), idx(2) have landed
     __syncthreads();         // every portion of tile 0 has landed
 
-    float mq[2] = {-INFINITY, -INFINITY};   // shared reference of head 32hh + 16j + r16
+    float mq[JT];   // shared reference of head 16*JT*hg + 16j + r16
+#pragma unroll
+    for (int j = 0; j < JT; j++) mq[j] = -INFINITY;
     for (int s = 0; s <= n; s++) {
       if (s < n) {
         const int par = s & 1;
@@ -170,25 +186,28 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
         if (new_seg) {
           // the first tile of a token starts a new segment; a later token's query is
           // loaded here (with it every DMA issued so far completes)
-          mq[0] = mq[1] = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < JT; j++) mq[j] = -INFINITY;
           if (s > 0) {
-            load_q2(cu.t, ln);
+            load_q(cu.t, ln);
             wait_vm<0>();
           }
         }
 
-        // ---- QK^T: rows 32rh + 16m + r16 (m = 0, 1) against heads 32hh + 16j + r16
-        const uint32_t vrow = sm.vmask[s % kST][2 * rh] | (sm.vmask[s % kST][2 * rh + 1] << 16);
-        f32x4 acc[2][2];
+        // ---- QK^T: rows 16*MT*rg + 16m + r16 against heads 16*JT*hg + 16j + r16
+        uint32_t vrow = 0;   // bit 16m + r: row 16*MT*rg + 16m + r is valid
 #pragma unroll
-        for (int m = 0; m < 2; m++)
+        for (int m = 0; m < MT; m++) vrow |= sm.vmask[s % kST][MT * rg + m] << (16 * m);
+        f32x4 acc[MT][JT];
 #pragma unroll
-          for (int j = 0; j < 2; j++) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        f16x2 sp[2][4];   // group scales of the lane's rows: sp[m][q] = groups 8g+2q, 8g+2q+1
+        for (int m = 0; m < MT; m++)
+#pragma unroll
+          for (int j = 0; j < JT; j++) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f16x2 sp[MT][4];   // group scales of the lane's rows: sp[m][q] = groups 8g+2q, 8g+2q+1
         if (vrow != 0) {
 #pragma unroll
-          for (int m = 0; m < 2; m++) {
-            const SMLA_LDS uint8_t* por = slot + (2 * rh + m) * kPortion + 16 * r16;
+          for (int m = 0; m < MT; m++) {
+            const SMLA_LDS uint8_t* por = slot + (MT * rg + m) * kPortion + 16 * r16;
             const u32x2 scb = lds_load<u32x2>(por + 256 * (16 + (g >> 1)) + 8 * (g & 1));
             sp[m][0] = e4m3x2<false>(scb.x);
             sp[m][1] = e4m3x2<true>(scb.x);
@@ -197,44 +216,44 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
           }
 #pragma unroll
           for (int kq = 0; kq < 4; kq++) {
-            u32x4 cw[2];
+            u32x4 cw[MT];
 #pragma unroll
-            for (int m = 0; m < 2; m++)
-              cw[m] = lds_load<u32x4>(slot + (2 * rh + m) * kPortion + 256 * (4 * g + kq) + 16 * r16);
+            for (int m = 0; m < MT; m++)
+              cw[m] = lds_load<u32x4>(slot + (MT * rg + m) * kPortion + 256 * (4 * g + kq) + 16 * r16);
 #pragma unroll
             for (int kk = 0; kk < 4; kk++) {
               const int k = 4 * kq + kk;
 #pragma unroll
-              for (int m = 0; m < 2; m++) {
+              for (int m = 0; m < MT; m++) {
                 const f16 sk = (k & 2) ? sp[m][k >> 2].y : sp[m][k >> 2].x;
                 const f16x8 a = unpack8(cw[m][kk], f16x2{sk, sk});
 #pragma unroll
-                for (int j = 0; j < 2; j++) acc[m][j] = mfma16x16x32(a, Q[j][k], acc[m][j]);
+                for (int j = 0; j < JT; j++) acc[m][j] = mfma16x16x32(a, Q[j][k], acc[m][j]);
               }
             }
           }
 #pragma unroll
-          for (int m = 0; m < 2; m++) {
-            const u32x4 rb = lds_load<u32x4>(slot + (2 * rh + m) * kPortion + 256 * (18 + g) + 16 * r16);
+          for (int m = 0; m < MT; m++) {
+            const u32x4 rb = lds_load<u32x4>(slot + (MT * rg + m) * kPortion + 256 * (18 + g) + 16 * r16);
             const f16x8 r0 = fp8x8(rb.x, rb.y), r1 = fp8x8(rb.z, rb.w);
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
+            for (int j = 0; j < JT; j++) {
               acc[m][j] = mfma16x16x32(r0, Q[j][16], acc[m][j]);
               acc[m][j] = mfma16x16x32(r1, Q[j][17], acc[m][j]);
             }
           }
         } else {
 #pragma unroll
-          for (int m = 0; m < 2; m++)
+          for (int m = 0; m < MT; m++)
 #pragma unroll
             for (int q = 0; q < 4; q++) sp[m][q] = f16x2{(f16)0.0f, (f16)0.0f};
         }
-        // PV scale table: the head-half-0 waves write their rows' scales (an empty row was
+        // PV scale table: the head-group-0 waves write their rows' scales (an empty row was
         // fetched as zeros, so its scales are 0)
-        if (hh == 0) {
+        if (hg == 0) {
 #pragma unroll
-          for (int m = 0; m < 2; m++) {
-            const int row = 32 * rh + 16 * m + r16;
+          for (int m = 0; m < MT; m++) {
+            const int row = 16 * MT * rg + 16 * m + r16;
 #pragma unroll
             for (int jj = 0; jj < 8; jj++)
               sm.sc[par][8 * g + jj][row] = (jj & 1) ? sp[m][jj >> 1].y : sp[m][jj >> 1].x;
@@ -247,28 +266,32 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
         issue_idx(cx, s + 4, ln);
         cx.next(cpt);
 
-        // ---- shared references after tile s-1 of the same segment: the larger one the row
-        // halves used
+        // ---- shared references after tile s-1 of the same segment: the largest one the
+        // row groups used
         if (s > 0 && !new_seg) {
           const int pp = par ^ 1;
           const int fl = sm.wflag[pp][0] | sm.wflag[pp][1] | sm.wflag[pp][2] | sm.wflag[pp][3];
           if (fl & 1) {
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-              const int h = 32 * hh + 16 * j + r16;
-              mq[j] = fmaxf(sm.wref[pp][0][h], sm.wref[pp][1][h]);
+            for (int j = 0; j < JT; j++) {
+              const int h = 16 * JT * hg + 16 * j + r16;
+              float m = sm.wref[pp][0][h];
+#pragma unroll
+              for (int q = 1; q < RG; q++) m = fmaxf(m, sm.wref[pp][q][h]);
+              mq[j] = m;
             }
           }
         }
 
-        // ---- softmax.  acc[m][j][jj] = score of row 32rh + 16m + 4g + jj, head 32hh + 16j + r16.
+        // ---- softmax.  acc[m][j][jj] = score of row 16*MT*rg + 16m + 4g + jj, head
+        // 16*JT*hg + 16j + r16.
         bool raised = false;
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-          float sv[2][4];
+        for (int j = 0; j < JT; j++) {
+          float sv[MT][4];
           float mx = -INFINITY;
 #pragma unroll
-          for (int m = 0; m < 2; m++)
+          for (int m = 0; m < MT; m++)
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) {
               sv[m][jj] = ((vrow >> (16 * m + 4 * g + jj)) & 1) ? acc[m][j][jj] * sl2 : -INFINITY;
@@ -277,16 +300,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
           mx = wave_max_xor16_32(mx);
           const float ref = (mx > mq[j] + kSlack) ? mx : mq[j];
           raised |= ref != mq[j];
-          const int h = 32 * hh + 16 * j + r16;
+          const int h = 16 * JT * hg + 16 * j + r16;
 #pragma unroll
-          for (int m = 0; m < 2; m++) {
+          for (int m = 0; m < MT; m++) {
             f16 p[4];
 #pragma unroll
             for (int jj = 0; jj < 4; jj++)
               p[jj] = (sv[m][jj] == -INFINITY) ? (f16)0.0f : (f16)__builtin_amdgcn_exp2f(sv[m][jj] - ref);
-            lds_store<f16x4>(&sm.pb[par][h][32 * rh + 16 * m + 4 * g], f16x4{p[0], p[1], p[2], p[3]});
+            lds_store<f16x4>(&sm.pb[par][h][16 * MT * rg + 16 * m + 4 * g], f16x4{p[0], p[1], p[2], p[3]});
           }
-          sm.wref[par][rh][h] = ref;
+          sm.wref[par][rg][h] = ref;
         }
         const bool wave_raised = __ballot(raised) != 0;
         sm.wflag[par][wid] = (wave_raised ? 1 : 0) | (vrow != 0 ? 2 : 0);
@@ -300,10 +323,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
     const int pw = wid - kWaves;   // output features 128pw .. 128pw + 127
     // O[tau][j4]: O^T for features 128pw + 16tau + 4g .. +3 of head 16*j4 + r16.
     // m_ref[j4], l_acc[j4]: reference and the lane's share of the denominator of that head.
-    f32x4 O[8][4];
-    float m_ref[4], l_acc[4];
+    f32x4 O[8][NJ];
+    float m_ref[NJ], l_acc[NJ];
 #pragma unroll
-    for (int j4 = 0; j4 < 4; j4++) {
+    for (int j4 = 0; j4 < NJ; j4++) {
 #pragma unroll
       for (int k = 0; k < 8; k++) O[k][j4] = f32x4{0.f, 0.f, 0.f, 0.f};
       m_ref[j4] = -INFINITY;
@@ -319,23 +342,26 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
         const int par = (s - 1) & 1;
         const SMLA_LDS uint8_t* const slot = ring + ((s - 1) % kST) * kSlot;
         const int ln = fresh_lane(lane), r16 = ln & 15, g = ln >> 4;
-        // ---- PV operand: probabilities of all 64 heads (rows 8g..8g+7 and 32+8g..)
+        // ---- PV operand: probabilities of all NH heads, rows 8g..8g+7 (half 0) and
+        // 32+8g.. (half 1); those rows belong to row group rgh[half]
         const int fl = sm.wflag[par][0] | sm.wflag[par][1] | sm.wflag[par][2] | sm.wflag[par][3];
-        f16x8 bop[4][2];
+        f16x8 bop[NJ][2];
 #pragma unroll
-        for (int j4 = 0; j4 < 4; j4++) {
+        for (int j4 = 0; j4 < NJ; j4++) {
           bop[j4][0] = lds_load<f16x8>(&sm.pb[par][16 * j4 + r16][8 * g]);
           bop[j4][1] = lds_load<f16x8>(&sm.pb[par][16 * j4 + r16][32 + 8 * g]);
         }
         if (fl & 1) {
-          // a row half raised its reference: the new shared reference of a head is the
-          // larger one used; rescale the accumulators, and the probabilities computed
+          // a row group raised its reference: the new shared reference of a head is the
+          // largest one used; rescale the accumulators, and the probabilities computed
           // against a smaller one
+          const int rgh[2] = {(8 * g) / (64 / RG), (32 + 8 * g) / (64 / RG)};
 #pragma unroll
-          for (int j4 = 0; j4 < 4; j4++) {
+          for (int j4 = 0; j4 < NJ; j4++) {
             const int h = 16 * j4 + r16;
-            const float q0 = sm.wref[par][0][h], q1 = sm.wref[par][1][h];
-            const float mnew = fmaxf(q0, q1);
+            float mnew = sm.wref[par][0][h];
+#pragma unroll
+            for (int q = 1; q < RG; q++) mnew = fmaxf(mnew, sm.wref[par][q][h]);
             if (mnew != m_ref[j4]) {
               const float alpha = __builtin_amdgcn_exp2f(m_ref[j4] - mnew);   // 0 if m_ref = -inf
 #pragma unroll
@@ -343,18 +369,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
               l_acc[j4] *= alpha;
               m_ref[j4] = mnew;
             }
-            if (q0 != mnew) {
-              const f16 e = (f16)__builtin_amdgcn_exp2f(q0 - mnew);
-              bop[j4][0] *= f16x8{e, e, e, e, e, e, e, e};
-            }
-            if (q1 != mnew) {
-              const f16 e = (f16)__builtin_amdgcn_exp2f(q1 - mnew);
-              bop[j4][1] *= f16x8{e, e, e, e, e, e, e, e};
+#pragma unroll
+            for (int half = 0; half < 2; half++) {
+              const float qh = sm.wref[par][rgh[half]][h];
+              if (qh != mnew) {
+                const f16 e = (f16)__builtin_amdgcn_exp2f(qh - mnew);
+                bop[j4][half] *= f16x8{e, e, e, e, e, e, e, e};
+              }
             }
           }
         }
 #pragma unroll
-        for (int j4 = 0; j4 < 4; j4++) l_acc[j4] += sum8(bop[j4][0]) + sum8(bop[j4][1]);
+        for (int j4 = 0; j4 < NJ; j4++) l_acc[j4] += sum8(bop[j4][0]) + sum8(bop[j4][1]);
 
         // ---- PV: O^T[128pw + 16tau + feature][head] += V^T P^T over the tile's 64 rows.
         // 4-bit transpose read: lane s of group g supplies tile row 8g+s (s < 8) or
@@ -371,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
             const f16x8 sc1 = lds_load<f16x8>(&sm.sc[par][tau][32 + 8 * g]);
             const f16x8 a0 = unpack8_pairs(d.x, sc0), a1 = unpack8_pairs(d.y, sc1);
 #pragma unroll
-            for (int j4 = 0; j4 < 4; j4++) {
+            for (int j4 = 0; j4 < NJ; j4++) {
               O[k][j4] = mfma16x16x32(a0, bop[j4][0], O[k][j4]);
               O[k][j4] = mfma16x16x32(a1, bop[j4][1], O[k][j4]);
             }
@@ -386,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
           const int seg = (t == t_first) ? 0 : 1;
           const int64_t slot_id = ((int64_t)hb * G + w) * 2 + seg;
 #pragma unroll
-          for (int j4 = 0; j4 < 4; j4++) {
+          for (int j4 = 0; j4 < NJ; j4++) {
             const float Ls = wave_sum_xor16_32(l_acc[j4]);
             const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
             const float lse_nat = Ls > 0.0f ? (m_ref[j4] + log2f(Ls)) * kLn2 : -INFINITY;
@@ -400,10 +426,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
               }
               if (pw == 0 && g == 0) A.lse[t * A.H + head0 + hl] = lse_nat;
             } else {
-              const uint32_t po = (uint32_t)((slot_id * kH + hl) * kLatent) * 4u;
+              const uint32_t po = (uint32_t)((slot_id * NH + hl) * kLatent) * 4u;
 #pragma unroll
               for (int k = 0; k < 8; k++) merge_st4(ws_o, po + 4u * (16 * (8 * pw + k) + 4 * g), O[k][j4] * inv);
-              if (pw == 0 && g == 0) merge_st1(ws_l, (uint32_t)(slot_id * kH + hl) * 4u, lse_nat);
+              if (pw == 0 && g == 0) merge_st1(ws_l, (uint32_t)(slot_id * NH + hl) * 4u, lse_nat);
             }
 #pragma unroll
             for (int k = 0; k < 8; k++) O[k][j4] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -419,8 +445,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
 
   // ---- publish this range's partials and merge the tokens whose last range this is.
   // The range's tokens: the first and the last may be shared with other ranges (partial),
-  // every other one lies inside it.  The two teams of four waves merge 32 heads each; the
-  // ring is idle from here on (every DMA has completed) and serves as their scratch.
+  // every other one lies inside it.  The ring is idle from here on (every DMA has
+  // completed) and serves as the merge's scratch.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (n <= 0) return;
@@ -431,7 +457,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
     if (partial(t0)) pend_t[0] = t0;
     if (t1 != t0 && partial(t1)) pend_t[1] = t1;
   }
+  constexpr int kTeamHeads = NH == 64 ? 32 : 16;   // heads merged by each active team
   const int team = tid >> 8, tt = tid & 255;
+  const bool active = NH == 64 || team == 0;
   float* const scratch = (float*)sm.ring + 2048 * team;
 #pragma unroll
   for (int seg = 0; seg < 2; seg++) {
@@ -454,20 +482,24 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_h64_kernel(Deco
     // starts before the token
     const uint32_t sl0 = (uint32_t)(((int64_t)hb * G + w_lo) * 2);
     const uint32_t seg0 = (wg_first_chunk(w_lo, C, G) < tok0) ? 1u : 0u;
+    const uint32_t h_off = active ? (uint32_t)(kTeamHeads * team) : 0u;
     auto part = [&](int s, uint32_t* o_off, uint32_t* l_off) {
       const uint32_t sl = sl0 + 2u * (uint32_t)s + (s == 0 ? seg0 : 0u);
-      *o_off = (sl * (uint32_t)kH + 32u * team) * (uint32_t)(kLatent * 4);
-      *l_off = (sl * (uint32_t)kH + 32u * team) * 4u;
+      *o_off = (sl * (uint32_t)NH + h_off) * (uint32_t)(kLatent * 4);
+      *l_off = (sl * (uint32_t)NH + h_off) * 4u;
     };
-    lse_merge<2 * kHeadGroup, true>((int)(w_hi - w_lo + 1), ws_o, ws_l, part,
-                                    (f16*)A.out + (t * A.H + head0 + 32 * team) * kLatent,
-                                    A.lse + t * A.H + head0 + 32 * team, scratch, tt);
+    lse_merge<kTeamHeads, true>((int)(w_hi - w_lo + 1), ws_o, ws_l, part,
+                                (f16*)A.out + (t * A.H + head0 + h_off) * kLatent,
+                                A.lse + t * A.H + head0 + h_off, scratch, tt, active);
     __syncthreads();
   }
 }
 
-hipError_t launch_decode_nvfp4_h64(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(sparse_mla_decode_h64_kernel, dim3(a.G * a.HB), dim3(kThreads), 0, s, a);
+hipError_t launch_decode_nvfp4_ws(const DecodeArgs& a, hipStream_t s, int heads) {
+  if (heads == 64)
+    hipLaunchKernelGGL(sparse_mla_decode_ws_kernel<64>, dim3(a.G * a.HB), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(sparse_mla_decode_ws_kernel<16>, dim3(a.G * a.HB), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

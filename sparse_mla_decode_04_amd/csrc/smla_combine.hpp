@@ -47,6 +47,9 @@ __device__ __forceinline__ void merge_st1(__amdgpu_buffer_rsrc_t r, uint32_t off
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 16);
 }
 
+// active = false: the thread does no work but passes the same barriers (a team that
+// shares the workgroup with the merging one).
+//
 // part(s, &o_off, &l_off): byte offsets of split s's O[NH][512] within the buffer of `ro`
 // and of its lse[NH] within the buffer of `rl`.  out: head 0 of the block (head stride 512
 // fp16); lse_out: head 0.  scratch: >= 2048 floats of LDS.
@@ -103,18 +106,108 @@ __device__ __forceinline__ void lse_merge_few(int ns, __amdgpu_buffer_rsrc_t ro,
   }
 }
 
+// Up to 2U splits (U = 4 for 16 heads, 2 for 32): the LSEs of every split (one value per
+// thread) and the output pieces of the first U splits in one memory round trip; the
+// per-head maximum, denominator and split weights through LDS; the output pieces of the
+// other splits in a second round trip.
+template <int NH, int U, bool kCoherent, class PartFn>
+__device__ __forceinline__ void lse_merge_two(int ns, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
+                                              PartFn part, f16* out, float* lse_out, float* scratch, int tid,
+                                              bool active) {
+  constexpr int P = NH / 2;             // 16-byte pieces per thread: piece q is head 2q + tid / 128
+  static_assert(2 * U * NH <= 256, "one LSE per thread");
+  float* const ls = scratch;            // [2U][NH] LSEs (-inf beyond ns)
+  float* const wt = scratch + 256;      // [2U][NH] weights
+  float* const mh = scratch + 512;      // [NH] maximum
+  float* const ih = scratch + 512 + NH; // [NH] 1 / denominator
+  const int h1 = tid >> 7;
+  f32x4 ov[U][P];
+  if (active) {
+    float x = -INFINITY;
+    if (tid < ns * NH) {
+      uint32_t o_off, l_off;
+      part(tid / NH, &o_off, &l_off);
+      x = merge_ld1<kCoherent>(rl, l_off + 4u * (tid % NH));
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {   // ns > U: every one of these splits exists
+      uint32_t o_off, l_off;
+      part(u, &o_off, &l_off);
+#pragma unroll
+      for (int q = 0; q < P; q++) ov[u][q] = merge_ld4<kCoherent>(ro, o_off + 16u * (256 * q + tid));
+    }
+    if (tid < 2 * U * NH) ls[tid] = x;
+  }
+  __syncthreads();
+  if (active && tid < NH) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 2 * U; s++) m = fmaxf(m, ls[s * NH + tid]);
+    float d = 0.0f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < 2 * U; s++) {
+        const float l = ls[s * NH + tid];
+        if (l != -INFINITY) d += __expf(l - m);
+      }
+    }
+    mh[tid] = m;
+    ih[tid] = d > 0.0f ? 1.0f / d : 0.0f;
+    lse_out[tid] = d > 0.0f ? m + logf(d) : -INFINITY;
+  }
+  __syncthreads();
+  if (active && tid < 2 * U * NH) {
+    const int h = tid % NH;
+    const float l = ls[tid];
+    wt[tid] = (l == -INFINITY) ? 0.0f : __expf(l - mh[h]) * ih[h];
+  }
+  __syncthreads();
+  if (!active) return;
+  f32x4 acc[P];
+#pragma unroll
+  for (int q = 0; q < P; q++) {
+    acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U; u++) acc[q] += wt[u * NH + 2 * q + h1] * ov[u][q];
+  }
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const int s = U + u;
+    uint32_t o_off, l_off;
+    part(s < ns ? s : 0, &o_off, &l_off);
+#pragma unroll
+    for (int q = 0; q < P; q++) ov[u][q] = merge_ld4<kCoherent>(ro, o_off + 16u * (256 * q + tid));
+  }
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    if (U + u >= ns) continue;
+#pragma unroll
+    for (int q = 0; q < P; q++) acc[q] += wt[(U + u) * NH + 2 * q + h1] * ov[u][q];
+  }
+#pragma unroll
+  for (int q = 0; q < P; q++) {
+    const int e = 256 * q + tid, h = e / 128, col = 4 * (e % 128);
+    *(f16x4*)(out + 512 * h + col) = f16x4{(f16)acc[q].x, (f16)acc[q].y, (f16)acc[q].z, (f16)acc[q].w};
+  }
+}
+
 template <int NH, bool kCoherent, class PartFn>
 __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
-                                          PartFn part, f16* out, float* lse_out, float* scratch, int tid) {
+                                          PartFn part, f16* out, float* lse_out, float* scratch, int tid,
+                                          bool active = true) {
   static_assert(NH == 16 || NH == 32, "head block");
   constexpr int kFew = NH == 16 ? 4 : 2;
+  constexpr int U = NH == 16 ? 4 : 2;  // splits per batch of output loads
   if (ns <= kFew) {
-    lse_merge_few<NH, kFew, kCoherent>(ns, ro, rl, part, out, lse_out, tid);
+    if (active) lse_merge_few<NH, kFew, kCoherent>(ns, ro, rl, part, out, lse_out, tid);
+    return;
+  }
+  if (ns <= 2 * U) {
+    lse_merge_two<NH, U, kCoherent>(ns, ro, rl, part, out, lse_out, scratch, tid, active);
     return;
   }
   constexpr int K = 256 / NH;          // threads per head in phase 1
   constexpr int P = NH / 2;            // 16-byte pieces per thread per split (NH*512*4 / 4096)
-  constexpr int U = NH == 16 ? 4 : 2;  // splits per batch of output loads
   constexpr int CS = 32;               // splits per chunk of weights
   float* const red = scratch;                 // [2][256] phase-1 partials
   float* const mh = scratch + 512;            // [NH] maximum
@@ -122,7 +215,7 @@ __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __a
   float* const wt = scratch + 1024;           // [CS][NH] weights of a chunk
 
   // ---- phase 1: thread (h, k) folds splits k, k+K, ...
-  {
+  if (active) {
     const int h = tid % NH, k = tid / NH;
     float m = -INFINITY, d = 0.0f;
     for (int s0 = 0; s0 < ns; s0 += 4 * K) {
@@ -150,7 +243,7 @@ __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __a
     red[256 + tid] = d;
   }
   __syncthreads();
-  if (tid < NH) {
+  if (active && tid < NH) {
     float m = -INFINITY;
 #pragma unroll
     for (int k = 0; k < K; k++) m = fmaxf(m, red[k * NH + tid]);
@@ -175,7 +268,7 @@ __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __a
   for (int q = 0; q < P; q++) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < ns; c0 += CS) {
     const int cn = min(CS, ns - c0);
-    for (int e = tid; e < cn * NH; e += 256) {
+    for (int e = tid; active && e < cn * NH; e += 256) {
       const int s = e / NH, h = e - s * NH;
       uint32_t o_off, l_off;
       part(c0 + s, &o_off, &l_off);
@@ -183,7 +276,7 @@ __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __a
       wt[e] = (ls == -INFINITY) ? 0.0f : __expf(ls - mh[h]) * ih[h];
     }
     __syncthreads();
-    for (int s0 = 0; s0 < cn; s0 += U) {
+    for (int s0 = 0; active && s0 < cn; s0 += U) {
       f32x4 ov[U][P];
 #pragma unroll
       for (int u = 0; u < U; u++) {
@@ -201,6 +294,7 @@ __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __a
     }
     __syncthreads();
   }
+  if (!active) return;
 #pragma unroll
   for (int q = 0; q < P; q++) {
     const int e = 256 * q + tid, h = e / 128, col = 4 * (e % 128);

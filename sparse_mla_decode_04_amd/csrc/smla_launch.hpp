@@ -15,13 +15,13 @@ hipError_t launch_unpack(const void* pool, int64_t pool_rows, const int32_t* row
 hipError_t launch_stage_fp8(const void* pool, int64_t pool_rows, const int32_t* idx,
                             int64_t entries, void* staged, hipStream_t s);
 // Decode workgroups resident per CU for the kernel variant of this shape (LDS budget).
-int decode_wgs_per_cu(bool fp8rows, int32_t NG);
-// NVFP4 decode: 64-head blocks use decode_h64.hip, 32-head blocks the LDS-ring kernel;
-// 16-head blocks the register-gather kernel (decode_regs.hip, variant 1) or the LDS-ring
-// kernel (variant 0).
+int decode_wgs_per_cu(bool fp8rows, int32_t NG, int variant);
+// NVFP4 decode: 64-head blocks use the role-specialised kernel (decode_ws.hip), 32-head
+// blocks the LDS-ring kernel; 16-head blocks the register-gather kernel (decode_regs.hip,
+// variant 1), the LDS-ring kernel (variant 0) or the role-specialised kernel (variant 2).
 hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s, int variant);
 hipError_t launch_decode_nvfp4_regs(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_decode_nvfp4_h64(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_nvfp4_ws(const DecodeArgs& a, hipStream_t s, int heads);
 hipError_t launch_decode_fp8rows(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t T, int32_t S,
                           int32_t H, void* out, float* lse, hipStream_t s);

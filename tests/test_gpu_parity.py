@@ -160,7 +160,7 @@ def test_decode_matches_oracle(smla, T, H, N, K, ef, seed):
     assert_parity(out, lse, ref_out, ref_lse, f"T{T} H{H} K{K}")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 17, 1000])
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 8, 17, 40, 56, 1000])
 def test_decode_every_split_count(smla, splits):
     _say("splits", splits)
     wl, src, q, idx = _setup(7, 16, 6000, 1000, 0.1, 11)
@@ -170,7 +170,18 @@ def test_decode_every_split_count(smla, splits):
     assert_parity(out, lse, ref_out, ref_lse, f"splits {splits}")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 8, 1000])
+@pytest.mark.parametrize("splits", [6, 10, 12, 24])
+def test_decode_every_split_count_32_heads(smla, splits):
+    # 32 tiles per token, so these give merges of 2 .. 9 splits
+    _say("splits 32 heads", splits)
+    wl, src, q, idx = _setup(3, 32, 5000, 2048, 0.05, 19)
+    pool = build_device_pool(src, DEV)
+    out, lse = _run_decode(smla, q, pool, idx, wl.softmax_scale, num_splits=splits)
+    ref_out, ref_lse = oracle.sparse_mla_decode_ref(q, OracleRows(src), idx, wl.softmax_scale)
+    assert_parity(out, lse, ref_out, ref_lse, f"32 heads splits {splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 20, 30, 1000])
 def test_decode_every_split_count_64_heads(smla, splits):
     _say("splits 64 heads", splits)
     wl, src, q, idx = _setup(5, 64, 6000, 900, 0.1, 18)
