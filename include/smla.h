@@ -174,6 +174,52 @@ SMLA_API int sparse_mla_decode_fp8rows(const void* q_dev, const void* staged_dev
                               int32_t num_splits, void* workspace_dev, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Grouped decode, step 1: union lists of token groups.  "Prime Intellect Launches Prime
+ * Inference, Serving 600B Tokens Daily" (sections on the agent workload and on the
+ * four-bit caches): the decode tokens of one agent session select largely the same cache
+ * rows, so a session's rows can be loaded once for all of its tokens.
+ *   indices_dev  int32 [T][topk] per-token lists as for sparse_mla_decode (negative or
+ *                >= pool_rows = empty).  No list may name a row twice (the union counts a
+ *                (row, token) pair once).
+ *   tpg          tokens per group, 1..4; T % tpg == 0.  Group g is tokens tpg*g .. +tpg-1.
+ *   U            capacity of a union list (entries per group).
+ *   union_dev    int32 [T/tpg][U] out: the rows some token of the group lists, each once,
+ *                in order of first occurrence reading the group's lists token by token;
+ *                entry = row | members << 27 (bit i of members: token i lists the row);
+ *                entries past the union's size are -1.
+ *   count_dev    int32 [T/tpg] out: the union's size.  A union larger than U keeps its
+ *                first U entries; count still reports the full size.
+ * Requires tpg * topk <= 8192 and pool_rows <= 2^27 (SMLA_ERR_UNSUPPORTED otherwise).
+ * Deterministic for lists without repeated rows.
+ */
+SMLA_API int smla_group_union(const int32_t* indices_dev, int32_t T, int32_t topk, int32_t tpg,
+                              int64_t pool_rows, int32_t U, int32_t* union_dev, int32_t* count_dev,
+                              void* stream);
+
+/*
+ * Grouped decode, step 2: sparse MLA decode of T tokens over the union lists of their
+ * groups.  Each cache row is gathered and unpacked once per group and applied to the heads
+ * of every token of the group; a score counts only where that token lists the row, so the
+ * result is that of sparse_mla_decode on the tokens' own lists (for lists without repeated
+ * rows), up to summation order.
+ *   q_dev, out_dev, lse_dev as in sparse_mla_decode ([T][H][576], [T][H][512], [T][H]).
+ *   union_dev    int32 [T/tpg][U] from smla_group_union (or any lists of that form).
+ *   tpg * H must be 64 (e.g. 4 tokens of 16 heads); pool_rows <= 2^27.
+ *   num_splits   0 = automatic; else workgroups sharing the (group, tile) sequence.
+ *   workspace    at least smla_decode_grouped_workspace_bytes(T, H, tpg, U, num_splits)
+ *                bytes, zero-filled before first use; left clean by every call.
+ */
+SMLA_API int sparse_mla_decode_grouped(const void* q_dev, const void* kv_pool_dev, int64_t pool_rows,
+                                       const int32_t* union_dev, int32_t T, int32_t H, int32_t tpg,
+                                       int32_t U, float softmax_scale, void* out_dev, float* lse_dev,
+                                       int32_t num_splits, void* workspace_dev, size_t workspace_bytes,
+                                       void* stream);
+
+/* Workspace bytes sparse_mla_decode_grouped needs (0 for a shape it rejects, or T == 0). */
+SMLA_API size_t smla_decode_grouped_workspace_bytes(int32_t T, int32_t H, int32_t tpg, int32_t U,
+                                                    int32_t num_splits);
+
 #ifdef __cplusplus
 }
 #endif

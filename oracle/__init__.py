@@ -28,6 +28,8 @@ Modules:
                dequantizer (unpack), the FP8 staging quantizer.
   attention -- sparse MLA decode over an index list, the log-sum-exp merge of
                partial results, and the staged FP8-row variant.
+  grouping  -- union lists of token groups and decode over them (the tokens of
+               one agent session sharing most of their rows).
 
 Every function is pinned by tests under tests/ (test_oracle_*.py) against
 values that do not come from the oracle itself: hand-typed format tables,
@@ -44,3 +46,4 @@ from .formats import (  # noqa: F401
 from .attention import (  # noqa: F401
     sparse_mla_decode_ref, lse_combine_ref, sparse_mla_decode_fp8rows_ref, dense_rows_for,
 )
+from .grouping import group_union_ref, sparse_mla_decode_grouped_ref  # noqa: F401

@@ -37,6 +37,10 @@ _SIGS = {
     "sparse_mla_combine": ([_P, _P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "nvfp4_stage_fp8": ([_P, _I64, _P, _I32, _I32, _P, _P], ctypes.c_int),
     "sparse_mla_decode_fp8rows": ([_P, _P, _P, _I64, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P], ctypes.c_int),
+    "smla_group_union": ([_P, _I32, _I32, _I32, _I64, _I32, _P, _P, _P], ctypes.c_int),
+    "sparse_mla_decode_grouped": ([_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P],
+                                  ctypes.c_int),
+    "smla_decode_grouped_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -238,3 +242,59 @@ def prepare_pack(src, slots, kv_pool):
             _check(st, "nvfp4_pack_rows")
     call.tensors = keep
     return call
+
+
+# ---------------------------------------------------------------- grouped decode ---
+
+def group_union(indices, tpg, pool_rows, U, union=None, count=None):
+    """Union lists of groups of `tpg` consecutive tokens: (union int32 [T/tpg, U],
+    count int32 [T/tpg]); entries are row | members << 27, -1 past the union's size."""
+    if indices.dim() != 2:
+        raise ValueError("indices must be int32 [T, topk]")
+    T, topk = indices.shape
+    if T % tpg != 0:
+        raise ValueError("T must be a multiple of tpg")
+    G = T // tpg
+    if union is None:
+        union = torch.empty((G, U), dtype=torch.int32, device=indices.device)
+    if count is None:
+        count = torch.empty((G,), dtype=torch.int32, device=indices.device)
+    _check(lib().smla_group_union(_dev(indices, "indices", torch.int32), T, topk, tpg, int(pool_rows), U,
+                                  _dev(union, "union", torch.int32, (G, U)), _dev(count, "count", torch.int32, (G,)),
+                                  _stream()), "smla_group_union")
+    return union, count
+
+
+def grouped_workspace_bytes(T, H, tpg, U, num_splits=0):
+    return int(lib().smla_decode_grouped_workspace_bytes(T, H, tpg, U, num_splits))
+
+
+def make_grouped_workspace(T, H, tpg, U, num_splits=0, device="cuda"):
+    """Zero-filled workspace for sparse_mla_decode_grouped (uint8 tensor)."""
+    nb = grouped_workspace_bytes(T, H, tpg, U, num_splits)
+    return torch.zeros(max(nb, 16), dtype=torch.uint8, device=device)
+
+
+def sparse_mla_decode_grouped(q, kv_pool, union, tpg, softmax_scale, out=None, lse=None, num_splits=0,
+                              workspace=None):
+    """Grouped decode over union lists: q fp16 [T, H, 576], union int32 [T/tpg, U]."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be fp16 [T, H, 576]")
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_BYTES:
+        raise ValueError("kv_pool must be uint8 [N, 352]")
+    T, H, _ = q.shape
+    U = union.shape[1]
+    if out is None:
+        out = torch.empty((T, H, LATENT_DIM), dtype=torch.float16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_grouped_workspace(T, H, tpg, U, num_splits, q.device)
+    _check(lib().sparse_mla_decode_grouped(
+        _dev(q, "q", torch.float16), _dev(kv_pool, "kv_pool", torch.uint8), kv_pool.shape[0],
+        _dev(union, "union", torch.int32, (T // tpg, U)), T, H, tpg, U, float(softmax_scale),
+        _dev(out, "out", torch.float16, (T, H, LATENT_DIM)), _dev(lse, "lse", torch.float32, (T, H)),
+        int(num_splits), _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream()),
+        "sparse_mla_decode_grouped")
+    return out, lse
+

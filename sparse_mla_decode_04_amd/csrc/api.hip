@@ -54,10 +54,10 @@ int cu_count() {
 // number of ranges, aligned to its tiles (so each range writes at most one partial and a
 // token's merge reads few of them), one workgroup per CU.  Otherwise the stream-K ranges
 // fill every resident workgroup slot once.
-int32_t auto_splits(bool fp8rows, int32_t T, int32_t H, int32_t topk) {
+int32_t auto_splits(bool fp8rows, int32_t T, int32_t H, int32_t topk, bool grouped = false) {
   const int64_t cpt = (topk + kTileRows - 1) / kTileRows;
   const int64_t C = (int64_t)T * cpt;
-  const int NG = heads_per_block_groups(H, topk, fp8rows);
+  const int NG = heads_per_block_groups(H, topk, fp8rows, grouped);
   const int64_t HB = H / (kHeadGroup * NG);
   const int64_t cus = cu_count();
   int64_t G;
@@ -68,7 +68,7 @@ int32_t auto_splits(bool fp8rows, int32_t T, int32_t H, int32_t topk) {
     if (S < 1) S = 1;
     G = (int64_t)T * S;
   } else {
-    G = cus * decode_wgs_per_cu(fp8rows, NG, decode_variant()) / HB;
+    G = cus * (grouped ? 1 : decode_wgs_per_cu(fp8rows, NG, decode_variant())) / HB;
     const int64_t cap = C / kMinTilesPerWg;
     if (G > cap) G = cap;
   }
@@ -94,9 +94,13 @@ int check_decode(const void* q, const void* rows, int64_t pool_rows, const int32
   return SMLA_OK;
 }
 
+// fp8rows: staged pass 2.  tok_heads > 0: grouped decode, with T groups of 64 heads made of
+// the heads of 64 / tok_heads tokens, and union-list entries in idx.
 int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
                const int32_t* idx, int32_t T, int32_t H, int32_t topk, float softmax_scale,
-               void* out, float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
+               void* out, float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream,
+               int32_t tok_heads = 0) {
+  const bool grouped = tok_heads > 0;
   int st = check_decode(q, rows, pool_rows, idx, T, H, topk, softmax_scale, out, lse, num_splits);
   if (st != SMLA_OK || T == 0) return st;
   // every buffer the kernels address through a buffer resource must fit its byte range
@@ -106,8 +110,8 @@ int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
   if (idx_bytes > kMaxBufferBytes || rows_bytes > kMaxBufferBytes || q_bytes > kMaxBufferBytes)
     return SMLA_ERR_UNSUPPORTED;
   if ((int64_t)T * ((topk + kTileRows - 1) / kTileRows) >= (int64_t)1 << 31) return SMLA_ERR_UNSUPPORTED;
-  const int32_t G = num_splits > 0 ? num_splits : auto_splits(fp8rows, T, H, topk);
-  const DecodePlan p = make_plan(T, H, topk, G, fp8rows);
+  const int32_t G = num_splits > 0 ? num_splits : auto_splits(fp8rows, T, H, topk, grouped);
+  const DecodePlan p = make_plan(T, H, topk, G, fp8rows, grouped);
   if (p.bytes > kMaxBufferBytes) return SMLA_ERR_UNSUPPORTED;
   if (p.bytes > 0 && (ws == nullptr || ws_bytes < p.bytes || !aligned16(ws))) return SMLA_ERR_WORKSPACE;
   DecodeArgs a;
@@ -133,9 +137,17 @@ int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
   a.counters = (int32_t*)((char*)ws + p.counters_off);
   a.part_o_bytes = (uint32_t)(p.part_lse_off - p.part_o_off);
   a.part_lse_bytes = (uint32_t)(p.counters_off - p.part_lse_off);
-  const hipError_t e = fp8rows ? launch_decode_fp8rows(a, (hipStream_t)stream)
-                               : launch_decode_nvfp4(a, (hipStream_t)stream, decode_variant());
+  a.tok_heads = tok_heads;
+  const hipError_t e = grouped ? launch_decode_grouped(a, (hipStream_t)stream)
+                       : fp8rows ? launch_decode_fp8rows(a, (hipStream_t)stream)
+                                 : launch_decode_nvfp4(a, (hipStream_t)stream, decode_variant());
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+// Grouped decode shapes: tpg tokens of H heads per group make the 64 heads of one block.
+bool grouped_shape_ok(int32_t T, int32_t H, int32_t tpg, int32_t U) {
+  return T >= 0 && H > 0 && tpg >= 1 && tpg <= kMaxGroupTokens && U >= 1 && U <= kMaxTopk &&
+         T % tpg == 0;
 }
 
 }  // namespace
@@ -226,6 +238,35 @@ SMLA_API int sparse_mla_decode_fp8rows(const void* q, const void* staged, const 
                               void* ws, size_t ws_bytes, void* stream) {
   return run_decode(true, q, staged, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
                     num_splits, ws, ws_bytes, stream);
+}
+
+SMLA_API int smla_group_union(const int32_t* idx, int32_t T, int32_t topk, int32_t tpg, int64_t pool_rows,
+                              int32_t U, int32_t* uni, int32_t* count, void* stream) {
+  if (T < 0 || tpg < 1 || tpg > kMaxGroupTokens || topk < 1 || U < 1 || pool_rows < 0 || T % tpg != 0)
+    return SMLA_ERR_INVALID_ARG;
+  if ((int64_t)tpg * topk > kMaxGroupEntries || pool_rows > (int64_t)kRowMask + 1) return SMLA_ERR_UNSUPPORTED;
+  if (T == 0) return SMLA_OK;
+  if (!idx || !uni || !count || !aligned4(idx) || !aligned4(uni) || !aligned4(count)) return SMLA_ERR_INVALID_ARG;
+  return launch_group_union(idx, T, topk, tpg, pool_rows, U, uni, count, (hipStream_t)stream) == hipSuccess
+             ? SMLA_OK
+             : SMLA_ERR_LAUNCH;
+}
+
+SMLA_API size_t smla_decode_grouped_workspace_bytes(int32_t T, int32_t H, int32_t tpg, int32_t U,
+                                                    int32_t num_splits) {
+  if (!grouped_shape_ok(T, H, tpg, U) || H * tpg != 4 * kHeadGroup || T == 0 || num_splits < 0) return 0;
+  const int32_t G = num_splits > 0 ? num_splits : auto_splits(false, T / tpg, 4 * kHeadGroup, U, true);
+  return make_plan(T / tpg, 4 * kHeadGroup, U, G, false, true).bytes;
+}
+
+SMLA_API int sparse_mla_decode_grouped(const void* q, const void* pool, int64_t pool_rows, const int32_t* uni,
+                                       int32_t T, int32_t H, int32_t tpg, int32_t U, float softmax_scale,
+                                       void* out, float* lse, int32_t num_splits, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  if (!grouped_shape_ok(T, H, tpg, U)) return SMLA_ERR_INVALID_ARG;
+  if (H * tpg != 4 * kHeadGroup || pool_rows > (int64_t)kRowMask + 1) return SMLA_ERR_UNSUPPORTED;
+  return run_decode(false, q, pool, pool_rows, uni, T / tpg, 4 * kHeadGroup, U, softmax_scale, out, lse,
+                    num_splits, ws, ws_bytes, stream, H);
 }
 
 }  // extern "C"

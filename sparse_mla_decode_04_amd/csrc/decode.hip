@@ -460,12 +460,14 @@ int decode_wgs_per_cu(bool fp8rows, int32_t NG, int variant) {
 }
 
 hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s, int variant) {
-  if (a.HB * 4 * kHeadGroup == a.H) return launch_decode_nvfp4_ws(a, s, 64);
+  if (a.HB * 4 * kHeadGroup == a.H) return launch_decode_nvfp4_ws(a, s, 64, false);
   if (a.HB * 2 * kHeadGroup == a.H) return launch_variant<2, 3, false, 1>(a, s);
   if (variant == 1) return launch_decode_nvfp4_regs(a, s);
-  if (variant == 2) return launch_decode_nvfp4_ws(a, s, 16);
+  if (variant == 2) return launch_decode_nvfp4_ws(a, s, 16, false);
   return launch_variant<1, 2, false, 2>(a, s);
 }
+
+hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t s) { return launch_decode_nvfp4_ws(a, s, 64, true); }
 
 hipError_t launch_decode_fp8rows(const DecodeArgs& a, hipStream_t s) {
   return (a.HB * 2 * kHeadGroup == a.H) ? launch_variant<2, 2, true, 1>(a, s)

@@ -58,6 +58,7 @@ struct WsShape {
 template <int NH>
 struct __attribute__((aligned(16))) SmemWs {
   uint8_t ring[kST][kSlot];               // [slot][portion][piece][row] 16-byte pieces
+  uint8_t members[kST][kTileRows];        // grouped decode: member bits of each row [slot][row]
   int32_t idx[2][kWaves][kWR];            // index-list DMA landing zone [tile parity][portion]
   f16 sc[2][32][kPH];                     // PV scales [parity][group][tile row]
   f16 pb[2][NH][kPH];                     // probabilities [parity][head][tile row]
@@ -77,7 +78,10 @@ __device__ __forceinline__ int fresh_lane(int lane) {
 
 }  // namespace
 
-template <int NH>
+// kGrouped: the index entries are union-list entries of token groups (row | members << 27),
+// the NH = 64 heads are those of the group's tokens (A.tok_heads heads each), and a score
+// counts only where the head's token lists the row.
+template <int NH, bool kGrouped>
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(DecodeArgs A) {
   using S = WsShape<NH>;
   constexpr int JT = S::JT, RG = S::RG, MT = S::MT, NJ = S::NJ;
@@ -122,8 +126,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
     auto issue_rows = [&](const Cursor& cur, int i, int ln) {
       const int r16 = ln & 15, g = ln >> 4;
       const int k = cur.ci * kTileRows + kWR * wid + r16;
-      const int32_t v = idxbuf[((i & 1) * kWaves + wid) * kWR + r16];
+      const int32_t e = idxbuf[((i & 1) * kWaves + wid) * kWR + r16];
+      const int32_t v = kGrouped ? (e < 0 ? -1 : (e & kRowMask)) : e;
       const bool ok = cur.c < c_hi && k < A.topk && row_valid(v, A.pool_rows);
+      if (kGrouped && g == 0) sm.members[i % kST][kWR * wid + r16] = ok ? (uint8_t)(e >> kMemberShift) : 0;
       const uint32_t base = (uint32_t)v * (uint32_t)kRowBytes;
       const uint32_t lds0 = lds_addr(ring + (i % kST) * kSlot + wid * kPortion);
 #pragma unroll
@@ -198,6 +204,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
         uint32_t vrow = 0;   // bit 16m + r: row 16*MT*rg + 16m + r is valid
 #pragma unroll
         for (int m = 0; m < MT; m++) vrow |= sm.vmask[s % kST][MT * rg + m] << (16 * m);
+        // grouped: byte jj of mrow[m] holds the member bits of row 16*MT*rg + 16m + 4g + jj
+        uint32_t mrow[MT];
+        if constexpr (kGrouped) {
+#pragma unroll
+          for (int m = 0; m < MT; m++)
+            mrow[m] = lds_load<uint32_t>(&sm.members[s % kST][16 * MT * rg + 16 * m + 4 * g]);
+        }
         f32x4 acc[MT][JT];
 #pragma unroll
         for (int m = 0; m < MT; m++)
@@ -290,11 +303,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
         for (int j = 0; j < JT; j++) {
           float sv[MT][4];
           float mx = -INFINITY;
+          // grouped: the token (within the group) of heads 16*JT*hg + 16j ..
+          const int tok = kGrouped ? (16 * JT * hg + 16 * j) / A.tok_heads : 0;
 #pragma unroll
           for (int m = 0; m < MT; m++)
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) {
-              sv[m][jj] = ((vrow >> (16 * m + 4 * g + jj)) & 1) ? acc[m][j][jj] * sl2 : -INFINITY;
+              bool valid = (vrow >> (16 * m + 4 * g + jj)) & 1;
+              if constexpr (kGrouped) valid = valid && ((mrow[m] >> (8 * jj + tok)) & 1);
+              sv[m][jj] = valid ? acc[m][j][jj] * sl2 : -INFINITY;
               mx = fmaxf(mx, sv[m][jj]);
             }
           mx = wave_max_xor16_32(mx);
@@ -495,11 +512,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
   }
 }
 
-hipError_t launch_decode_nvfp4_ws(const DecodeArgs& a, hipStream_t s, int heads) {
-  if (heads == 64)
-    hipLaunchKernelGGL(sparse_mla_decode_ws_kernel<64>, dim3(a.G * a.HB), dim3(kThreads), 0, s, a);
+hipError_t launch_decode_nvfp4_ws(const DecodeArgs& a, hipStream_t s, int heads, bool grouped) {
+  const dim3 grid(a.G * a.HB), block(kThreads);
+  if (grouped)
+    hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<64, true>), grid, block, 0, s, a);
+  else if (heads == 64)
+    hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<64, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(sparse_mla_decode_ws_kernel<16>, dim3(a.G * a.HB), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<16, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

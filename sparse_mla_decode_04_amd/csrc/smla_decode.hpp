@@ -23,6 +23,15 @@ namespace smla {
 constexpr int kTileRows = 64;    // index-list entries per tile
 constexpr int kHeadGroup = 16;   // heads per MFMA tile
 
+// Grouped decode (the tokens of a session share most of their list entries): each group of
+// up to kMaxGroupTokens consecutive tokens attends over one union list whose entries are
+// row | (members << kMemberShift); bit i of members says that token i of the group lists
+// the row.  A negative entry is empty.
+constexpr int kMemberShift = 27;
+constexpr int32_t kRowMask = (1 << kMemberShift) - 1;
+constexpr int kMaxGroupTokens = 4;
+constexpr int kMaxGroupEntries = 8192;   // tokens per group x topk the union builder takes
+
 struct DecodeArgs {
   const void* q;            // fp16 [T][H][576]
   const void* rows;         // NVFP4 pool [pool_rows][352], or staged FP8 rows [T*topk][576]
@@ -42,6 +51,7 @@ struct DecodeArgs {
   float* part_o;            // fp32 [HB][G][2][16*NG][512]
   float* part_lse;          // fp32 [HB][G][2][16*NG]
   int32_t* counters;        // [HB][T], zero between launches
+  int32_t tok_heads;        // grouped decode: heads per real token (entries carry membership bits); else 0
   uint32_t part_o_bytes;    // bytes of part_o
   uint32_t part_lse_bytes;  // bytes of part_lse
 };
@@ -64,18 +74,20 @@ __host__ __device__ inline int64_t wg_of_chunk(int64_t c, int64_t C, int64_t G) 
 // Head groups of 16 per workgroup.  The unpack of a row is shared by all heads of a block,
 // so blocks are as large as the head count allows: 64 heads (NVFP4 rows only), else 32,
 // else 16.  Blocks of 32 or 64 need a token to span at least two tiles (those kernels
-// stage one query at a time).
-inline int32_t heads_per_block_groups(int32_t H, int32_t topk, bool fp8rows) {
+// stage one query at a time).  Grouped decode always runs 64-head blocks (the heads of
+// the tokens of one group).
+inline int32_t heads_per_block_groups(int32_t H, int32_t topk, bool fp8rows, bool grouped = false) {
+  if (grouped) return 4;
   if (topk <= kTileRows) return 1;
   if (!fp8rows && H % (4 * kHeadGroup) == 0) return 4;
   return H % (2 * kHeadGroup) == 0 ? 2 : 1;
 }
 
-inline DecodePlan make_plan(int32_t T, int32_t H, int32_t topk, int32_t G, bool fp8rows) {
+inline DecodePlan make_plan(int32_t T, int32_t H, int32_t topk, int32_t G, bool fp8rows, bool grouped = false) {
   DecodePlan p;
   p.cpt = (topk + kTileRows - 1) / kTileRows;
   p.tiles = (int64_t)T * p.cpt;
-  p.NG = heads_per_block_groups(H, topk, fp8rows);
+  p.NG = heads_per_block_groups(H, topk, fp8rows, grouped);
   p.HB = H / (kHeadGroup * p.NG);
   if (G > p.tiles) G = (int32_t)p.tiles;
   if (G < 1) G = 1;

@@ -21,7 +21,12 @@ int decode_wgs_per_cu(bool fp8rows, int32_t NG, int variant);
 // variant 1), the LDS-ring kernel (variant 0) or the role-specialised kernel (variant 2).
 hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s, int variant);
 hipError_t launch_decode_nvfp4_regs(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_decode_nvfp4_ws(const DecodeArgs& a, hipStream_t s, int heads);
+hipError_t launch_decode_nvfp4_ws(const DecodeArgs& a, hipStream_t s, int heads, bool grouped);
+// Grouped decode: the role-specialised kernel on union lists of token groups.
+hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t s);
+// Union lists of token groups (group.hip).
+hipError_t launch_group_union(const int32_t* idx, int32_t T, int32_t topk, int32_t tpg, int64_t pool_rows,
+                              int32_t U, int32_t* uni, int32_t* count, hipStream_t s);
 hipError_t launch_decode_fp8rows(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t T, int32_t S,
                           int32_t H, void* out, float* lse, hipStream_t s);

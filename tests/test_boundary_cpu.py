@@ -88,3 +88,30 @@ def test_python_binding_rejects_host_tensors():
     with pytest.raises((ValueError, TypeError)):
         smla.nvfp4_pack_rows(torch.zeros(2, 576, dtype=torch.float16), torch.zeros(2, dtype=torch.int32),
                              torch.zeros(4, 352, dtype=torch.uint8))
+
+
+def test_grouped_entry_points_check_arguments(L):
+    # union builder: tpg out of range, T not a multiple of tpg, too many entries, huge pool
+    assert L.smla_group_union(P(16), 8, 64, 0, 100, 64, P(16), P(16), None) == -1
+    assert L.smla_group_union(P(16), 8, 64, 5, 100, 64, P(16), P(16), None) == -1
+    assert L.smla_group_union(P(16), 6, 64, 4, 100, 64, P(16), P(16), None) == -1
+    assert L.smla_group_union(P(16), 8, 4096, 4, 100, 64, P(16), P(16), None) == -2
+    assert L.smla_group_union(P(16), 8, 64, 4, 1 << 28, 64, P(16), P(16), None) == -2
+    assert L.smla_group_union(P(16), 8, 64, 4, 100, 0, P(16), P(16), None) == -1
+    assert L.smla_group_union(None, 8, 64, 4, 100, 64, P(16), P(16), None) == -1
+    assert L.smla_group_union(None, 0, 64, 4, 100, 64, None, None, None) == 0      # nothing to do
+    # grouped decode: tpg * H must be 64
+    args = dict(q=16, pool=16, uni=16, T=8, H=16, tpg=4, U=128, out=16, lse=16)
+
+    def dec(**kw):
+        a = dict(args, **kw)
+        return L.sparse_mla_decode_grouped(P(a["q"]), P(a["pool"]), 100, P(a["uni"]), a["T"], a["H"], a["tpg"],
+                                           a["U"], 0.1, P(a["out"]), P(a["lse"]), 0, None, 0, None)
+    assert dec(H=32) == -2
+    assert dec(tpg=3, T=9) == -2
+    assert dec(T=6) == -1
+    assert dec(U=0) == -1
+    assert dec(q=None) == -1
+    assert dec() == -3                                   # workspace missing
+    assert smla.grouped_workspace_bytes(264, 16, 4, 3584) > 0
+    assert smla.grouped_workspace_bytes(264, 16, 3, 3584) == 0
