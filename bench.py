@@ -155,6 +155,78 @@ def staged_timing(binding, wl, layers, q_d, idx_d, out, lse, ws, fused_ms, steps
             "fused_speedup": (p1 + p2) / (fused_ms * 1e3), "steps": steps}
 
 
+def grouped_timing(binding, wl, layers, q, q_d, idx, idx_d, src_full, kv_bytes, fused_ms, steps, check_tokens):
+    """Session-grouped decode: the tokens of a session (64/H consecutive tokens) share
+    most of their rows; smla_group_union builds each group's union list (member bits per
+    row) on the GPU, sparse_mla_decode_grouped loads every union row once for all of the
+    group's tokens.  Both launches are timed with events on the launch stream; the union
+    capacity U is the largest union of the workload's lists rounded up to a tile."""
+    import torch
+    import oracle
+    from helpers import OracleRows, parity_errors
+    tpg = 64 // wl.H
+    if tpg * wl.H != 64 or wl.T % tpg:
+        return None
+    sizes = []
+    for g in range(wl.T // tpg):
+        v = idx[g * tpg:(g + 1) * tpg].reshape(-1)
+        sizes.append(len(np.unique(v[(v >= 0) & (v < wl.pool_rows)])))
+    U = -(-max(sizes) // 64) * 64
+    uniq_rows = int(sum(sizes))
+    G = wl.T // tpg
+    uni = torch.empty((G, U), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((G,), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.T, wl.H, 512), dtype=torch.float16, device="cuda")
+    lse = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
+    ws = binding.make_grouped_workspace(wl.T, wl.H, tpg, U, 0, "cuda")
+    L = len(layers)
+
+    def run(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        binding.group_union(idx_d, tpg, wl.pool_rows, U, uni, cnt)
+        if ev is not None:
+            ev[1].record()
+        binding.sparse_mla_decode_grouped(q_d, layers[i % L], uni, tpg, wl.softmax_scale, out, lse, 0, ws)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    assert int(cnt.max().item()) <= U
+    res = {"tokens_per_group": tpg, "union_capacity": U, "union_rows": uniq_rows,
+           "unique_kv_bytes": uniq_rows * 352}
+    if check_tokens > 0:
+        rng = np.random.default_rng(1)
+        toks = sorted(rng.choice(wl.T, size=min(wl.T, check_tokens), replace=False).tolist())
+        ref_o, ref_l = oracle.sparse_mla_decode_ref(q, OracleRows(src_full), idx, wl.softmax_scale, tokens=toks)
+        oe, le, ok = parity_errors(out.cpu().numpy()[toks], lse.cpu().numpy()[toks], ref_o, ref_l)
+        log(f"grouped parity on tokens {toks}: out err {oe:.2e}, lse err {le:.2e}, -inf ok {ok}")
+        if not (oe <= 2e-3 and le <= 1e-3 and ok):
+            print("bench.py: grouped decode does not match the oracle", file=sys.stderr)
+            sys.exit(3)
+        res["parity"] = {"tokens": toks, "out_err": oe, "lse_err": le}
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for i in range(steps):
+        run(3 + i, evs[i])
+    torch.cuda.synchronize()
+    u_us = float(np.mean([a.elapsed_time(b) for a, b, c in evs])) * 1e3
+    d_us = float(np.mean([b.elapsed_time(c) for a, b, c in evs])) * 1e3
+    tot = u_us + d_us
+    res.update({"union_us": u_us, "decode_us": d_us, "us_per_launch": tot, "steps": steps,
+                "gathered_kv_GBs": kv_bytes / (tot * 1e-6) / 1e9,
+                "unique_kv_GBs_decode": uniq_rows * 352 / (d_us * 1e-6) / 1e9,
+                "per_token_us": fused_ms * 1e3, "speedup": fused_ms * 1e3 / tot})
+    log(f"session-grouped ({tpg} tokens/group, union {uniq_rows} rows = {uniq_rows * 352 / 1e6:.1f} MB of "
+        f"{kv_bytes / 1e6:.1f} MB gathered): union {u_us:.1f} us + decode {d_us:.1f} us = {tot:.1f} us "
+        f"vs per-token {fused_ms * 1e3:.1f} us; {res['gathered_kv_GBs']:.0f} GB/s on gathered KV, "
+        f"{res['unique_kv_GBs_decode']:.0f} GB/s on unique rows in the decode")
+    del uni, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(nbytes=256 << 20, reps=5):
     """A copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch of this copy,
     against its 256 MiB read and 256 MiB written, give the factors that turn those counters
@@ -180,6 +252,9 @@ def main():
     ap.add_argument("--staged", type=int, default=-1,
                     help="also time the staged two-pass variant for this many steps "
                          "(default: 20 for the cache-write workload, else 0)")
+    ap.add_argument("--grouped", type=int, default=-1,
+                    help="also time session-grouped decode (union lists of groups of 64/H tokens, then "
+                         "one pass over them) for this many steps (default: 20 for the agent-mix workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -284,6 +359,9 @@ def main():
         log(f"cache write ({len(slots)} rows): mean {pack_us:.2f} us")
     staged_steps = args.staged if args.staged >= 0 else (20 if pack else 0)
     staged = staged_timing(binding, wl, layers, q_d, idx_d, out, lse, ws, k_avg, staged_steps) if staged_steps else None
+    grouped_steps = args.grouped if args.grouped >= 0 else (20 if wl.name == "agent_mix" else 0)
+    grouped = (grouped_timing(binding, wl, layers, q, q_d, idx, idx_d, src_full, kv_bytes, k_avg, grouped_steps,
+                              args.check_tokens) if grouped_steps else None)
 
     traffic = traffic_from_profiles(wl.name)
     flops = 2.0 * wl.H * (576 + 512) * n_valid        # QK^T over 576 + PV over 512, per valid entry
@@ -319,6 +397,8 @@ def main():
         res["config"]["cache_write_us"] = pack_us
     if staged:
         res["staged_variant"] = staged
+    if grouped:
+        res["session_grouped"] = grouped
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(wl, q, idx, src_full, args.cpu_seconds)
         log(f"cpu oracle: {res['cpu_baseline']['value']:.1f} tokens/s")
