@@ -32,6 +32,7 @@ constexpr int kThreadsU = 256;
 constexpr int kPerThread = kMaxGroupEntries / kThreadsU;   // 32 entries per thread, in order
 
 struct SmemU {
+  int32_t ent[kMaxGroupEntries];  // the group's list entries, read from memory once
   int32_t key[kSlots];          // row in the slot, or -1
   uint32_t mem[kSlots / 4];     // member bits, one byte per slot
   uint32_t claim[kSlots / 32];  // slot already placed in the output
@@ -75,6 +76,9 @@ __global__ __launch_bounds__(kThreadsU) void group_union_kernel(const int32_t* _
   const int ne = tpg * topk;   // entries of the group, <= kMaxGroupEntries
   const int32_t* lists = idx + g * tpg * (int64_t)topk;
 
+  // the entries (coalesced, all loads in flight together), cleared table
+#pragma unroll 8
+  for (int e = tid; e < ne; e += kThreadsU) sm.ent[e] = lists[e];
   for (int i = tid; i < kSlots; i += kThreadsU) sm.key[i] = -1;
   for (int i = tid; i < kSlots / 4; i += kThreadsU) sm.mem[i] = 0;
   for (int i = tid; i < kSlots / 32; i += kThreadsU) sm.claim[i] = 0;
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kThreadsU) void group_union_kernel(const int32_t* _
 
   // ---- insert every valid entry and its token's member bit
   for (int e = tid; e < ne; e += kThreadsU) {
-    const int32_t v = lists[e];
+    const int32_t v = sm.ent[e];
     if (v < 0 || v >= pool_rows) continue;
     const uint32_t h = insert_row(sm, v);
     atomicOr(&sm.mem[h >> 2], 1u << (8 * (h & 3) + e / topk));
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(kThreadsU) void group_union_kernel(const int32_t* _
   for (int q = 0; q < kPerThread; q++) {
     const int e = kPerThread * tid + q;
     if (e >= ne) break;
-    const int32_t v = lists[e];
+    const int32_t v = sm.ent[e];
     if (v < 0 || v >= pool_rows) continue;
     const int tok = e / topk;
     const uint32_t h = find_row(sm, v);
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(kThreadsU) void group_union_kernel(const int32_t* _
   for (int q = 0; q < kPerThread; q++) {
     if (!((keep >> q) & 1u)) continue;
     const int e = kPerThread * tid + q;
-    const int32_t v = lists[e];
+    const int32_t v = sm.ent[e];
     const uint32_t h = find_row(sm, v);
     const uint32_t members = (sm.mem[h >> 2] >> (8 * (h & 3))) & 0xFFu;
     if (pos < U) out[pos] = v | (int32_t)(members << kMemberShift);
