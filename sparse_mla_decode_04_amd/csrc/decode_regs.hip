@@ -186,16 +186,19 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   // reference and flags are issued by every lane (same value, same address): no branch,
   // so this code interleaves with the PV step of the previous tile.
   auto softmax = [&](const f32x4 (&acc)[2], uint32_t vm, int par, float m_cur) {
+    // exp2(score * scale_log2 - ref) in one fma each; an invalid row enters as -inf (exp2
+    // gives 0), a head with no valid row takes 0 for -ref; no mask when all rows are valid
     const f32x4 a = acc[0] + acc[1];
     float sv[4];
+    const bool all_valid = vm == 0xFFFFu;
 #pragma unroll
-    for (int jj = 0; jj < 4; jj++) sv[jj] = ((vm >> (4 * g + jj)) & 1) ? a[jj] * sl2 : -INFINITY;
-    const float mx = wave_max_xor16_32(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    for (int jj = 0; jj < 4; jj++) sv[jj] = (all_valid || ((vm >> (4 * g + jj)) & 1)) ? a[jj] : -INFINITY;
+    const float mx = wave_max_xor16_32(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])) * sl2);
     const float ref = (mx > m_cur + kSlack) ? mx : m_cur;
+    const float nref = (ref == -INFINITY) ? 0.0f : -ref;
     f16 p[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; jj++)
-      p[jj] = (sv[jj] == -INFINITY) ? (f16)0.0f : (f16)__builtin_amdgcn_exp2f(sv[jj] - ref);
+    for (int jj = 0; jj < 4; jj++) p[jj] = (f16)__builtin_amdgcn_exp2f(fmaf(sv[jj], sl2, nref));
     lds_store<f16x4>(&sm.pb[par][r16][kWR * wid + 4 * g], f16x4{p[0], p[1], p[2], p[3]});
     sm.wref[par][wid][r16] = ref;
     const bool wave_raised = __ballot(ref != m_cur) != 0;

@@ -298,32 +298,43 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
 
         // ---- softmax.  acc[m][j][jj] = score of row 16*MT*rg + 16m + 4g + jj, head
         // 16*JT*hg + 16j + r16.
+        // Scores enter as exp2(score * scale_log2 - ref) in one fma each; an invalid row
+        // enters as -inf (exp2 gives 0), and a head with no valid row takes 0 for -ref.
+        // When every row of the wave is valid (and no member bits apply) no mask is needed.
+        const bool all_valid = !kGrouped && vrow == (MT == 2 ? 0xFFFFFFFFu : 0xFFFFu);
         bool raised = false;
 #pragma unroll
         for (int j = 0; j < JT; j++) {
           float sv[MT][4];
-          float mx = -INFINITY;
           // grouped: the token (within the group) of heads 16*JT*hg + 16j ..
           const int tok = kGrouped ? (16 * JT * hg + 16 * j) / A.tok_heads : 0;
 #pragma unroll
           for (int m = 0; m < MT; m++)
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) {
-              bool valid = (vrow >> (16 * m + 4 * g + jj)) & 1;
-              if constexpr (kGrouped) valid = valid && ((mrow[m] >> (8 * jj + tok)) & 1);
-              sv[m][jj] = valid ? acc[m][j][jj] * sl2 : -INFINITY;
-              mx = fmaxf(mx, sv[m][jj]);
+              if (all_valid) {
+                sv[m][jj] = acc[m][j][jj];
+              } else {
+                bool valid = (vrow >> (16 * m + 4 * g + jj)) & 1;
+                if constexpr (kGrouped) valid = valid && ((mrow[m] >> (8 * jj + tok)) & 1);
+                sv[m][jj] = valid ? acc[m][j][jj] : -INFINITY;
+              }
             }
-          mx = wave_max_xor16_32(mx);
+          float mx = sv[0][0];
+#pragma unroll
+          for (int m = 0; m < MT; m++)
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) mx = fmaxf(mx, sv[m][jj]);
+          mx = wave_max_xor16_32(mx * sl2);   // scale_log2 > 0: the scaled maximum
           const float ref = (mx > mq[j] + kSlack) ? mx : mq[j];
           raised |= ref != mq[j];
+          const float nref = (ref == -INFINITY) ? 0.0f : -ref;
           const int h = 16 * JT * hg + 16 * j + r16;
 #pragma unroll
           for (int m = 0; m < MT; m++) {
             f16 p[4];
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++)
-              p[jj] = (sv[m][jj] == -INFINITY) ? (f16)0.0f : (f16)__builtin_amdgcn_exp2f(sv[m][jj] - ref);
+            for (int jj = 0; jj < 4; jj++) p[jj] = (f16)__builtin_amdgcn_exp2f(fmaf(sv[m][jj], sl2, nref));
             lds_store<f16x4>(&sm.pb[par][h][16 * MT * rg + 16 * m + 4 * g], f16x4{p[0], p[1], p[2], p[3]});
           }
           sm.wref[par][rg][h] = ref;
