@@ -25,9 +25,11 @@ once at the end (to fp16 for outputs).
 
 Modules:
   formats   -- E2M1 / E4M3 code tables, the NVFP4 row quantizer (pack) and
-               dequantizer (unpack), the FP8 staging quantizer.
+               dequantizer (unpack), the FP8 staging quantizer, the 576-byte
+               FP8 row writer and reader.
   attention -- sparse MLA decode over an index list, the log-sum-exp merge of
-               partial results, and the staged FP8-row variant.
+               partial results, the staged FP8-row variant, and decode over a
+               pool of 576-byte FP8 rows.
   grouping  -- union lists of token groups and decode over them (the tokens of
                one agent session sharing most of their rows).
 
@@ -38,12 +40,14 @@ product attention in float64, and closed-form identities.
 """
 
 from .formats import (  # noqa: F401
-    ROW_BYTES, LATENT_DIM, ROPE_DIM, HEAD_DIM, GROUP, CODE_BYTES, SCALE_BYTES, ROPE_BYTES,
+    ROW_BYTES, FP8_ROW_BYTES, LATENT_DIM, ROPE_DIM, HEAD_DIM, GROUP, CODE_BYTES, SCALE_BYTES, ROPE_BYTES,
     e2m1_value, e4m3_value, e2m1_table, e4m3_table,
     e4m3_encode, e4m3_encode_scaled_by, e2m1_encode,
     nvfp4_pack_rows_ref, nvfp4_unpack_rows_ref, fp8_stage_rows_ref,
+    fp8_pack_rows_ref, fp8_unpack_rows_ref,
 )
 from .attention import (  # noqa: F401
     sparse_mla_decode_ref, lse_combine_ref, sparse_mla_decode_fp8rows_ref, dense_rows_for,
+    sparse_mla_decode_fp8pool_ref,
 )
 from .grouping import group_union_ref, sparse_mla_decode_grouped_ref  # noqa: F401

@@ -30,7 +30,7 @@ Readings taken here where the page leaves the step open:
 import numpy as np
 
 from .formats import (HEAD_DIM, LATENT_DIM, ROW_BYTES, nvfp4_unpack_rows_ref,
-                      fp8_stage_rows_ref, e4m3_table)
+                      fp8_stage_rows_ref, fp8_unpack_rows_ref, e4m3_table)
 
 _E4M3 = e4m3_table()
 
@@ -120,4 +120,13 @@ def sparse_mla_decode_fp8rows_ref(q, pool, indices, softmax_scale, tokens=None):
     def rows_fn(ids):
         rows = np.asarray(pool[np.asarray(ids, dtype=np.int64)], dtype=np.uint8)
         return _E4M3[fp8_stage_rows_ref(rows)]
+    return sparse_mla_decode_ref(q, pool, indices, softmax_scale, tokens=tokens, rows_fn=rows_fn)
+
+
+def sparse_mla_decode_fp8pool_ref(q, pool, indices, softmax_scale, tokens=None):
+    """Decode over a pool of 576-byte FP8 rows (the cache format before NVFP4): the same
+    definition as sparse_mla_decode_ref, with K_j the E4M3 values of pool row idx[t, j].
+    `pool` maps an int64 id array to uint8 [n, 576] rows by indexing."""
+    def rows_fn(ids):
+        return fp8_unpack_rows_ref(np.asarray(pool[np.asarray(ids, dtype=np.int64)], dtype=np.uint8))
     return sparse_mla_decode_ref(q, pool, indices, softmax_scale, tokens=tokens, rows_fn=rows_fn)

@@ -21,6 +21,10 @@ Readings taken here where the page leaves the step open:
     E2M1 value (ties to the even code), saturating at 6, sign kept (so small
     negatives give the -0 code 0x8).  A zero scale gives code +-0 for all 16.
   * Rope values are rounded to nearest E4M3 (ties to even), saturating at 448.
+  * The FP8 cache row the page starts from (576 bytes) holds the 576 values of a
+    row as E4M3 codes, one byte each, value k in byte k (latent 0..511, rope
+    512..575), with no scale: each is the value rounded to nearest E4M3, ties to
+    even, saturating at 448.
 
 All arithmetic below is exact: decoded values are small dyadic rationals held
 exactly in float64, and every rounding decision compares an input against a
@@ -37,6 +41,7 @@ CODE_BYTES = LATENT_DIM // 2      # 256
 SCALE_BYTES = LATENT_DIM // GROUP  # 32
 ROPE_BYTES = ROPE_DIM             # 64
 ROW_BYTES = CODE_BYTES + SCALE_BYTES + ROPE_BYTES  # 352
+FP8_ROW_BYTES = HEAD_DIM          # 576: one E4M3 byte per value
 E4M3_MAX = 448.0
 E2M1_MAX = 6.0
 
@@ -221,3 +226,20 @@ def fp8_stage_rows_ref(rows):
     """
     vals = nvfp4_unpack_rows_ref(rows)
     return e4m3_encode(vals)
+
+
+def fp8_pack_rows_ref(src):
+    """Quantize fp16 rows [n, 576] into 576-byte FP8 cache rows [n, 576] (uint8):
+    byte k is the E4M3 code of value k (nearest, ties to even, saturating at 448)."""
+    src = np.asarray(src)
+    if src.dtype != np.float16 or src.ndim != 2 or src.shape[1] != HEAD_DIM:
+        raise ValueError("fp8_pack_rows_ref expects float16 [n, 576]")
+    return e4m3_encode(src.astype(np.float64))
+
+
+def fp8_unpack_rows_ref(rows):
+    """Decode 576-byte FP8 rows [n, 576] to exact values float64 [n, 576]."""
+    rows = np.asarray(rows)
+    if rows.dtype != np.uint8 or rows.ndim != 2 or rows.shape[1] != FP8_ROW_BYTES:
+        raise ValueError("fp8_unpack_rows_ref expects uint8 [n, 576]")
+    return _E4M3[rows]
