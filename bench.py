@@ -18,7 +18,9 @@ Prints one JSON line on stdout.  `value` is decode tokens per second of the
 whole step; `roofline` prices the decode kernel's gathered KV bytes (352 bytes
 per valid list entry) against its average launch duration measured with HIP
 events around each launch on the launch stream; `cpu_baseline` times the CPU
-oracle on the host on the same workload.
+oracle on the host on the same workload.  Untimed for `value`, side legs report
+the staged two-pass variant, session-grouped decode and (`fp8_pool`) the same
+decode over the pool kept as 576-byte FP8 rows, the format NVFP4 replaces.
 """
 
 import argparse
@@ -227,6 +229,56 @@ def grouped_timing(binding, wl, layers, q, q_d, idx, idx_d, src_full, kv_bytes, 
     return res
 
 
+def fp8pool_timing(binding, wl, q, q_d, idx, idx_d, src_full, n_valid, fused_ms, steps, check_tokens):
+    """Decode over the same pool kept as 576-byte FP8 rows (the format NVFP4 replaces):
+    the row writer encodes the fp16 source rows, layer copies span the same cold range,
+    and sparse_mla_decode_fp8pool is timed with events on the launch stream."""
+    import torch
+    import oracle
+    from helpers import OracleFp8Rows, build_device_fp8_pool, parity_errors
+    pool0 = build_device_fp8_pool(src_full, "cuda")
+    L = max(2, -(-COLD_SPAN_BYTES // pool0.numel()))
+    layers = [pool0] + [pool0.clone() for _ in range(L - 1)]
+    out = torch.empty((wl.T, wl.H, 512), dtype=torch.float16, device="cuda")
+    lse = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
+    ws = binding.make_workspace(wl.T, wl.H, wl.topk, 0, "cuda")
+
+    def run(i):
+        binding.sparse_mla_decode_fp8pool(q_d, layers[i % L], idx_d, wl.softmax_scale, out, lse, 0, ws)
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    kv8 = n_valid * 576
+    res = {"row_bytes": 576, "layer_copies": L, "gathered_kv_bytes": kv8}
+    if check_tokens > 0:
+        rng = np.random.default_rng(2)
+        toks = sorted(rng.choice(wl.T, size=min(wl.T, check_tokens), replace=False).tolist())
+        ref_o, ref_l = oracle.sparse_mla_decode_fp8pool_ref(q, OracleFp8Rows(src_full), idx, wl.softmax_scale,
+                                                            tokens=toks)
+        oe, le, ok = parity_errors(out.cpu().numpy()[toks], lse.cpu().numpy()[toks], ref_o, ref_l)
+        log(f"fp8 pool parity on tokens {toks}: out err {oe:.2e}, lse err {le:.2e}, -inf ok {ok}")
+        if not (oe <= 2e-3 and le <= 1e-3 and ok):
+            print("bench.py: FP8-pool decode does not match the oracle", file=sys.stderr)
+            sys.exit(3)
+        res["parity"] = {"tokens": toks, "out_err": oe, "lse_err": le}
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        run(3 + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    res.update({"us_per_launch": us, "steps": steps, "gathered_kv_GBs": kv8 / (us * 1e-6) / 1e9,
+                "nvfp4_us": fused_ms * 1e3, "nvfp4_speedup": us / (fused_ms * 1e3),
+                "rows_per_byte_vs_nvfp4": 352 / 576})
+    log(f"FP8 576-byte pool: {us:.1f} us per launch ({res['gathered_kv_GBs']:.0f} GB/s on {kv8 / 1e6:.1f} MB "
+        f"gathered) vs NVFP4 {fused_ms * 1e3:.1f} us; NVFP4 holds {576 / 352:.2f}x the rows per byte")
+    del layers, pool0, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(nbytes=256 << 20, reps=5):
     """A copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch of this copy,
     against its 256 MiB read and 256 MiB written, give the factors that turn those counters
@@ -255,6 +307,9 @@ def main():
     ap.add_argument("--grouped", type=int, default=-1,
                     help="also time session-grouped decode (union lists of groups of 64/H tokens, then "
                          "one pass over them) for this many steps (default: 20 for the agent-mix workload)")
+    ap.add_argument("--fp8pool", type=int, default=50,
+                    help="also time decode over the same pool kept as 576-byte FP8 rows for this many "
+                         "steps (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -363,6 +418,9 @@ def main():
     grouped = (grouped_timing(binding, wl, layers, q, q_d, idx, idx_d, src_full, kv_bytes, k_avg, grouped_steps,
                               args.check_tokens) if grouped_steps else None)
 
+    fp8pool = (fp8pool_timing(binding, wl, q, q_d, idx, idx_d, src_full, n_valid, k_avg, args.fp8pool,
+                              args.check_tokens) if args.fp8pool > 0 else None)
+
     traffic = traffic_from_profiles(wl.name)
     flops = 2.0 * wl.H * (576 + 512) * n_valid        # QK^T over 576 + PV over 512, per valid entry
     tflops = flops / (k_avg * 1e-3) / 1e12
@@ -399,6 +457,8 @@ def main():
         res["staged_variant"] = staged
     if grouped:
         res["session_grouped"] = grouped
+    if fp8pool:
+        res["fp8_pool"] = fp8pool
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(wl, q, idx, src_full, args.cpu_seconds)
         log(f"cpu oracle: {res['cpu_baseline']['value']:.1f} tokens/s")

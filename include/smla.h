@@ -135,8 +135,8 @@ SMLA_API int32_t smla_choose_num_splits(int32_t T, int32_t H, int32_t topk);
 
 /*
  * Workspace bytes sparse_mla_decode needs (num_splits as passed to it, 0 = automatic).
- * Also an upper bound for sparse_mla_decode_fp8rows with the same arguments, whose
- * automatic split count is never larger.
+ * Also an upper bound for sparse_mla_decode_fp8rows and sparse_mla_decode_fp8pool with
+ * the same arguments, whose automatic split count is never larger.
  */
 SMLA_API size_t smla_decode_workspace_bytes(int32_t T, int32_t H, int32_t topk, int32_t num_splits);
 
@@ -173,6 +173,32 @@ SMLA_API int sparse_mla_decode_fp8rows(const void* q_dev, const void* staged_dev
                               int32_t topk, float softmax_scale, void* out_dev, float* lse_dev,
                               int32_t num_splits, void* workspace_dev, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * FP8 cache rows, writer ("Four-bit caches make room": before NVFP4 a cache row was 576
+ * bytes of FP8).  Encodes n fp16 rows src_dev[n][576] and writes each as a 576-byte row
+ * at fp8_pool_dev + slots_dev[i] * 576: byte k = E4M3 code of value k (nearest, ties to
+ * even, saturating at 448, sign kept).  Rows whose slot is negative or >= pool_rows are
+ * skipped.  Inputs must be finite.  Slots must be distinct (two rows written to one slot
+ * race).  n == 0 enqueues nothing.
+ */
+SMLA_API int fp8_pack_rows(const void* src_dev, const int32_t* slots_dev, int32_t n, void* fp8_pool_dev,
+                           int64_t pool_rows, void* stream);
+
+/*
+ * Sparse MLA decode over a pool kept in that FP8 format: the capacity-for-latency trade
+ * the same section describes (576 instead of 352 bytes per row, no unpack beyond
+ * E4M3 -> fp16, which is exact).  fp8_pool_dev is uint8 [pool_rows][576] as written by
+ * fp8_pack_rows; indices_dev names its rows as for sparse_mla_decode (-1 or >= pool_rows
+ * = empty).  Every other argument, the result and the workspace rule are those of
+ * sparse_mla_decode (smla_decode_workspace_bytes gives the size); heads are processed in
+ * blocks of 32 or 16.  pool_rows * 576 may be at most 4 GiB - 4 KiB, else
+ * SMLA_ERR_UNSUPPORTED.
+ */
+SMLA_API int sparse_mla_decode_fp8pool(const void* q_dev, const void* fp8_pool_dev, int64_t pool_rows,
+                                       const int32_t* indices_dev, int32_t T, int32_t H, int32_t topk,
+                                       float softmax_scale, void* out_dev, float* lse_dev, int32_t num_splits,
+                                       void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
  * Grouped decode, step 1: union lists of token groups.  "Prime Intellect Launches Prime

@@ -37,6 +37,9 @@ _SIGS = {
     "sparse_mla_combine": ([_P, _P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
     "nvfp4_stage_fp8": ([_P, _I64, _P, _I32, _I32, _P, _P], ctypes.c_int),
     "sparse_mla_decode_fp8rows": ([_P, _P, _P, _I64, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P], ctypes.c_int),
+    "fp8_pack_rows": ([_P, _P, _I32, _P, _I64, _P], ctypes.c_int),
+    "sparse_mla_decode_fp8pool": ([_P, _P, _I64, _P, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P],
+                                  ctypes.c_int),
     "smla_group_union": ([_P, _I32, _I32, _I32, _I64, _I32, _P, _P, _P], ctypes.c_int),
     "sparse_mla_decode_grouped": ([_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P],
                                   ctypes.c_int),
@@ -148,6 +151,8 @@ def _decode_common(entry, q, rows, pool_rows, indices, softmax_scale, out, lse, 
             _dev(lse, "lse", torch.float32, (T, H)), int(num_splits), p_ws, workspace.numel(), _stream())
     if entry == "sparse_mla_decode":
         st = lib().sparse_mla_decode(p_q, rows, pool_rows, p_idx, *tail)
+    elif entry == "sparse_mla_decode_fp8pool":
+        st = lib().sparse_mla_decode_fp8pool(p_q, rows, pool_rows, p_idx, *tail)
     else:
         st = lib().sparse_mla_decode_fp8rows(p_q, rows, p_idx, pool_rows, *tail)
     _check(st, entry)
@@ -200,6 +205,26 @@ def sparse_mla_decode_fp8rows(q, staged, indices, pool_rows, softmax_scale, out=
     p_st = _dev(staged, "staged", torch.uint8, (T, topk, HEAD_DIM))
     return _decode_common("sparse_mla_decode_fp8rows", q, p_st, int(pool_rows), indices, softmax_scale,
                           out, lse, num_splits, workspace)
+
+
+def fp8_pack_rows(src, slots, fp8_pool):
+    """Encode fp16 rows src[n, 576] as 576-byte E4M3 rows of fp8_pool[N, 576] at slots[n]."""
+    n = src.shape[0] if src.dim() == 2 else -1
+    p_src = _dev(src, "src", torch.float16, (n, HEAD_DIM))
+    p_slots = _dev(slots, "slots", torch.int32, (n,))
+    if fp8_pool.dim() != 2 or fp8_pool.shape[1] != HEAD_DIM:
+        raise ValueError("fp8_pool must be uint8 [N, 576]")
+    p_pool = _dev(fp8_pool, "fp8_pool", torch.uint8)
+    _check(lib().fp8_pack_rows(p_src, p_slots, n, p_pool, fp8_pool.shape[0], _stream()), "fp8_pack_rows")
+
+
+def sparse_mla_decode_fp8pool(q, fp8_pool, indices, softmax_scale, out=None, lse=None, num_splits=0,
+                              workspace=None):
+    """Sparse MLA decode over a pool of 576-byte FP8 rows: (out fp16 [T, H, 512], lse fp32 [T, H])."""
+    if fp8_pool.dim() != 2 or fp8_pool.shape[1] != HEAD_DIM:
+        raise ValueError("fp8_pool must be uint8 [N, 576]")
+    return _decode_common("sparse_mla_decode_fp8pool", q, _dev(fp8_pool, "fp8_pool", torch.uint8),
+                          fp8_pool.shape[0], indices, softmax_scale, out, lse, num_splits, workspace)
 
 
 def prepare_decode(q, kv_pool, indices, softmax_scale, out, lse, num_splits=0, workspace=None):

@@ -94,19 +94,25 @@ int check_decode(const void* q, const void* rows, int64_t pool_rows, const int32
   return SMLA_OK;
 }
 
-// fp8rows: staged pass 2.  tok_heads > 0: grouped decode, with T groups of 64 heads made of
-// the heads of 64 / tok_heads tokens, and union-list entries in idx.
-int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
+// What `rows` holds: the NVFP4 pool, the staged FP8 rows of pass 2 (one per list entry),
+// or a pool of FP8 rows.
+enum class Rows { kNvfp4Pool, kFp8Staged, kFp8Pool };
+
+// tok_heads > 0: grouped decode, with T groups of 64 heads made of the heads of
+// 64 / tok_heads tokens, and union-list entries in idx.
+int run_decode(Rows kind, const void* q, const void* rows, int64_t pool_rows,
                const int32_t* idx, int32_t T, int32_t H, int32_t topk, float softmax_scale,
                void* out, float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream,
                int32_t tok_heads = 0) {
   const bool grouped = tok_heads > 0;
+  const bool fp8rows = kind != Rows::kNvfp4Pool;
   int st = check_decode(q, rows, pool_rows, idx, T, H, topk, softmax_scale, out, lse, num_splits);
   if (st != SMLA_OK || T == 0) return st;
   // every buffer the kernels address through a buffer resource must fit its byte range
   const uint64_t idx_bytes = (uint64_t)T * topk * 4;
   const uint64_t q_bytes = (uint64_t)T * H * 576 * 2;
-  const uint64_t rows_bytes = fp8rows ? (uint64_t)T * topk * 576 : (uint64_t)pool_rows * 352;
+  const uint64_t rows_bytes = kind == Rows::kFp8Staged ? (uint64_t)T * topk * 576
+                              : (uint64_t)pool_rows * (kind == Rows::kFp8Pool ? 576 : 352);
   if (idx_bytes > kMaxBufferBytes || rows_bytes > kMaxBufferBytes || q_bytes > kMaxBufferBytes)
     return SMLA_ERR_UNSUPPORTED;
   if ((int64_t)T * ((topk + kTileRows - 1) / kTileRows) >= (int64_t)1 << 31) return SMLA_ERR_UNSUPPORTED;
@@ -138,6 +144,7 @@ int run_decode(bool fp8rows, const void* q, const void* rows, int64_t pool_rows,
   a.part_o_bytes = (uint32_t)(p.part_lse_off - p.part_o_off);
   a.part_lse_bytes = (uint32_t)(p.counters_off - p.part_lse_off);
   a.tok_heads = tok_heads;
+  a.fp8_pool = kind == Rows::kFp8Pool;
   const hipError_t e = grouped ? launch_decode_grouped(a, (hipStream_t)stream)
                        : fp8rows ? launch_decode_fp8rows(a, (hipStream_t)stream)
                                  : launch_decode_nvfp4(a, (hipStream_t)stream, decode_variant());
@@ -202,7 +209,7 @@ SMLA_API size_t smla_decode_workspace_bytes(int32_t T, int32_t H, int32_t topk, 
 SMLA_API int sparse_mla_decode(const void* q, const void* pool, int64_t pool_rows, const int32_t* idx,
                       int32_t T, int32_t H, int32_t topk, float softmax_scale, void* out,
                       float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
-  return run_decode(false, q, pool, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
+  return run_decode(Rows::kNvfp4Pool, q, pool, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
                     num_splits, ws, ws_bytes, stream);
 }
 
@@ -236,7 +243,25 @@ SMLA_API int sparse_mla_decode_fp8rows(const void* q, const void* staged, const 
                               int64_t pool_rows, int32_t T, int32_t H, int32_t topk,
                               float softmax_scale, void* out, float* lse, int32_t num_splits,
                               void* ws, size_t ws_bytes, void* stream) {
-  return run_decode(true, q, staged, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
+  return run_decode(Rows::kFp8Staged, q, staged, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
+                    num_splits, ws, ws_bytes, stream);
+}
+
+SMLA_API int fp8_pack_rows(const void* src, const int32_t* slots, int32_t n, void* pool, int64_t pool_rows,
+                           void* stream) {
+  if (n < 0 || pool_rows < 0) return SMLA_ERR_INVALID_ARG;
+  if (n == 0) return SMLA_OK;
+  if (!src || !slots || !pool || !aligned16(src) || !aligned4(slots) || !aligned16(pool))
+    return SMLA_ERR_INVALID_ARG;
+  return launch_fp8_pack(src, slots, n, pool, pool_rows, (hipStream_t)stream) == hipSuccess ? SMLA_OK
+                                                                                            : SMLA_ERR_LAUNCH;
+}
+
+SMLA_API int sparse_mla_decode_fp8pool(const void* q, const void* pool, int64_t pool_rows, const int32_t* idx,
+                                       int32_t T, int32_t H, int32_t topk, float softmax_scale, void* out,
+                                       float* lse, int32_t num_splits, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  return run_decode(Rows::kFp8Pool, q, pool, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
                     num_splits, ws, ws_bytes, stream);
 }
 
@@ -265,8 +290,8 @@ SMLA_API int sparse_mla_decode_grouped(const void* q, const void* pool, int64_t 
                                        void* stream) {
   if (!grouped_shape_ok(T, H, tpg, U)) return SMLA_ERR_INVALID_ARG;
   if (H * tpg != 4 * kHeadGroup || pool_rows > (int64_t)kRowMask + 1) return SMLA_ERR_UNSUPPORTED;
-  return run_decode(false, q, pool, pool_rows, uni, T / tpg, 4 * kHeadGroup, U, softmax_scale, out, lse,
-                    num_splits, ws, ws_bytes, stream, H);
+  return run_decode(Rows::kNvfp4Pool, q, pool, pool_rows, uni, T / tpg, 4 * kHeadGroup, U, softmax_scale, out,
+                    lse, num_splits, ws, ws_bytes, stream, H);
 }
 
 }  // extern "C"

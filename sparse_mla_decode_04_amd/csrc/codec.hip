@@ -1,5 +1,5 @@
-// NVFP4 cache-row codec kernels for gfx950: the row writer (pack), the unpack export
-// used by tests, and pass 1 of the staged FP8 variant.
+// Cache-row codec kernels for gfx950: the NVFP4 row writer (pack), the unpack export
+// used by tests, pass 1 of the staged FP8 variant, and the 576-byte FP8 row writer.
 //
 // "Prime Intellect Launches Prime Inference, Serving 600B Tokens Daily", section
 // "Four-bit caches make room": NVFP4 (one FP8 scale per 16 four-bit values) is the
@@ -118,6 +118,41 @@ __global__ __launch_bounds__(256) void nvfp4_stage_fp8_kernel(const uint8_t* __r
   for (int k = 0; k < 4; k++) hi |= e4m3_encode_rne((float)v[4 + k]) << (8 * k);
   *(u32x2*)(o + 8 * lane) = u32x2{lo, hi};
   if (lane < 8) *(u32x2*)(o + kLatent + 8 * lane) = *(const u32x2*)(p + kRopeOff + 8 * lane);
+}
+
+// The 576-byte FP8 cache row (the format NVFP4 replaces in "Four-bit caches make room"):
+// byte k is the E4M3 code of value k.  One wave per row; lane l encodes the 8 values of
+// piece l (and lanes 0..7 also piece 64 + l, the rope part) and writes them as 8 bytes.
+__global__ __launch_bounds__(256) void fp8_pack_rows_kernel(const f16* __restrict__ src,
+                                                             const int32_t* __restrict__ slots, int32_t n,
+                                                             uint8_t* __restrict__ pool, int64_t pool_rows) {
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wid;
+  if (row >= n) return;
+  const int32_t slot = slots[row];
+  if (slot < 0 || (int64_t)slot >= pool_rows) return;
+  const f16* x = src + row * kHeadDim;
+  uint8_t* o = pool + (int64_t)slot * kHeadDim;
+  for (int p = lane; p < kHeadDim / 8; p += 64) {
+    const u32x4 v = *(const u32x4*)(x + 8 * p);
+    f16 h[8];
+    __builtin_memcpy(h, &v, 16);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      lo |= e4m3_encode_rne((float)h[k]) << (8 * k);
+      hi |= e4m3_encode_rne((float)h[4 + k]) << (8 * k);
+    }
+    *(u32x2*)(o + 8 * p) = u32x2{lo, hi};
+  }
+}
+
+hipError_t launch_fp8_pack(const void* src, const int32_t* slots, int32_t n, void* pool, int64_t pool_rows,
+                           hipStream_t s) {
+  const int blocks = (n + 3) / 4;
+  hipLaunchKernelGGL(fp8_pack_rows_kernel, dim3(blocks), dim3(256), 0, s, (const f16*)src, slots, n,
+                     (uint8_t*)pool, pool_rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const void* src, const int32_t* slots, int32_t n, void* pool,

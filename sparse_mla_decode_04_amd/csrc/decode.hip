@@ -55,9 +55,10 @@
 // every later token is staged into LDS by the same DMA path, issued just before the rows of
 // the token's first tile, and moved to registers at that tile.
 //
-// The same skeleton with kFp8 = true is pass 2 of the staged variant: it attends over
-// 576-byte FP8 E4M3 rows written to HBM by pass 1 (one per list entry), reading V^T
-// through the 8-bit LDS transpose read.
+// The same skeleton with kFp8 = true attends over 576-byte FP8 E4M3 rows, reading V^T
+// through the 8-bit LDS transpose read: either the rows pass 1 of the staged variant
+// wrote to HBM (one per list entry), or the rows of a pool kept in FP8 (entry v names
+// pool row v, as for NVFP4).
 #include "smla_launch.hpp"
 #include "smla_tile.hpp"
 
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256, WPC) void sparse_mla_decode_kernel(DecodeArgs 
     const bool ok = cur.c < c_hi && k < A.topk && row_valid(v, A.pool_rows);
     uint32_t base;
     if constexpr (kFp8)
-      base = (uint32_t)(cur.t * A.topk + k) * (uint32_t)kHeadDim;
+      base = (uint32_t)(A.fp8_pool ? v : cur.t * A.topk + k) * (uint32_t)kHeadDim;
     else
       base = (uint32_t)v * (uint32_t)kRowBytes;
     const uint32_t lds0 = lds_addr(ring + (i % ST) * F::kSlot + wid * F::kPortion);

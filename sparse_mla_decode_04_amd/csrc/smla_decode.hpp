@@ -34,7 +34,8 @@ constexpr int kMaxGroupEntries = 8192;   // tokens per group x topk the union bu
 
 struct DecodeArgs {
   const void* q;            // fp16 [T][H][576]
-  const void* rows;         // NVFP4 pool [pool_rows][352], or staged FP8 rows [T*topk][576]
+  const void* rows;         // NVFP4 pool [pool_rows][352], staged FP8 rows [T*topk][576],
+                            // or (fp8_pool) an FP8 pool [pool_rows][576]
   int64_t pool_rows;
   const int32_t* idx;       // [T][topk]
   int32_t T, H, topk;
@@ -54,6 +55,7 @@ struct DecodeArgs {
   int32_t tok_heads;        // grouped decode: heads per real token (entries carry membership bits); else 0
   uint32_t part_o_bytes;    // bytes of part_o
   uint32_t part_lse_bytes;  // bytes of part_lse
+  int32_t fp8_pool;         // FP8 rows: 1 = row v of a pool, 0 = the staged row of entry (t, j)
 };
 
 struct DecodePlan {

@@ -12,6 +12,8 @@ hipError_t launch_pack(const void* src, const int32_t* slots, int32_t n, void* p
                        int64_t pool_rows, hipStream_t s);
 hipError_t launch_unpack(const void* pool, int64_t pool_rows, const int32_t* rows, int32_t n,
                          void* out, hipStream_t s);
+hipError_t launch_fp8_pack(const void* src, const int32_t* slots, int32_t n, void* pool, int64_t pool_rows,
+                           hipStream_t s);
 hipError_t launch_stage_fp8(const void* pool, int64_t pool_rows, const int32_t* idx,
                             int64_t entries, void* staged, hipStream_t s);
 // Decode workgroups resident per CU for the kernel variant of this shape (LDS budget).

@@ -1,7 +1,7 @@
 """Shared glue for the GPU parity tests and the benchmark's checks: building a
-device pool through the library's own row writer, the oracle's view of the same
-pool (quantized from the same fp16 source rows by the oracle), and the parity
-tolerances."""
+device pool (NVFP4 or FP8 rows) through the library's own row writers, the
+oracle's view of the same pool (quantized from the same fp16 source rows by the
+oracle), and the parity tolerances."""
 
 import numpy as np
 
@@ -34,6 +34,33 @@ class OracleRows:
         import oracle
         ids = np.asarray(ids, dtype=np.int64)
         return oracle.nvfp4_pack_rows_ref(self.src[ids])
+
+
+class OracleFp8Rows:
+    """576-byte FP8 pool rows as the oracle sees them: encoded by the oracle's own FP8 row
+    writer from the fp16 source rows, built on demand for the requested row ids."""
+
+    def __init__(self, src):
+        self.src = src
+
+    def __getitem__(self, ids):
+        import oracle
+        ids = np.asarray(ids, dtype=np.int64)
+        return oracle.fp8_pack_rows_ref(self.src[ids])
+
+
+def build_device_fp8_pool(src, device, chunk=65536):
+    """Encode the fp16 source rows into a device pool of 576-byte FP8 rows with fp8_pack_rows."""
+    import torch
+    import sparse_mla_decode_04_amd as smla
+    N = src.shape[0]
+    pool = torch.zeros((N, 576), dtype=torch.uint8, device=device)
+    for a in range(0, N, chunk):
+        b = min(N, a + chunk)
+        s = torch.from_numpy(np.ascontiguousarray(src[a:b])).to(device)
+        slots = torch.arange(a, b, dtype=torch.int32, device=device)
+        smla.fp8_pack_rows(s, slots, pool)
+    return pool
 
 
 def build_device_pool(src, device, chunk=65536):

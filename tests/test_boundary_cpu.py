@@ -115,3 +115,21 @@ def test_grouped_entry_points_check_arguments(L):
     assert dec() == -3                                   # workspace missing
     assert smla.grouped_workspace_bytes(264, 16, 4, 3584) > 0
     assert smla.grouped_workspace_bytes(264, 16, 3, 3584) == 0
+
+
+def test_fp8pool_entry_points_check_arguments(L):
+    assert L.fp8_pack_rows(None, None, 0, None, 10, None) == 0          # n == 0: no-op
+    assert L.fp8_pack_rows(None, P(16), 3, P(16), 10, None) == -1
+    assert L.fp8_pack_rows(P(16), P(16), 3, P(8), 10, None) == -1        # misaligned pool
+    assert L.fp8_pack_rows(P(16), P(16), -1, P(16), 10, None) == -1
+
+    def dec(pool_rows=100, H=16, q=16):
+        return L.sparse_mla_decode_fp8pool(P(q), P(16), pool_rows, P(16), 2, H, 64, 0.1, P(16), P(16), 0,
+                                           None, 0, None)
+    assert dec(q=None) == -1
+    assert dec(H=24) == -2
+    assert dec() == -3                                   # workspace missing
+    # 8M rows of 576 bytes exceed one buffer resource's 4 GiB range; as NVFP4 rows they fit
+    assert dec(pool_rows=8_000_000) == -2
+    assert L.sparse_mla_decode(P(16), P(16), 8_000_000, P(16), 2, 16, 64, 0.1, P(16), P(16), 0,
+                               None, 0, None) == -3

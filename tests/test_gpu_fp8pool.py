@@ -1,0 +1,126 @@
+"""GPU parity of the 576-byte FP8 cache format (called through the C ABI) against the
+CPU oracle: the row writer fp8_pack_rows bit-exact against oracle.fp8_pack_rows_ref,
+and sparse_mla_decode_fp8pool within the decode tolerance (max |out - ref| <= 2e-3
+max |ref|, |lse - ref| <= 1e-3, -inf exactly where the oracle has it) against
+oracle.sparse_mla_decode_fp8pool_ref: head blocks of 16 and 32, several tiles with a
+ragged tail, empty and out-of-range entries, empty tokens, every kind of split; and at
+the full sizes of the 35- and 264-token workloads on sampled tokens."""
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_mla_decode_04_amd import workloads as W
+from helpers import OracleFp8Rows, assert_parity, build_device_fp8_pool, pool_source_all
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fp8_row_layout_example.json")
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def smla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_mla_decode_04_amd as m
+    m.lib()
+    return m
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def test_fp8_pack_bit_exact(smla):
+    _say("fp8 pack")
+    rng = np.random.default_rng(3)
+    n, N = 300, 400
+    src = (rng.standard_normal((n, 576)) * np.exp(rng.uniform(-10, 7, (n, 576)))).astype(np.float16)
+    ex = json.load(open(GOLDEN))
+    for k, v in ex["values"].items():               # the hand-worked row: ties, saturation, -0
+        src[0, int(k)] = float(v)
+    src[1, :] = 0
+    src[1, ::3] = np.float16(-0.0)
+    slots = rng.permutation(N)[:n].astype(np.int32)
+    slots[5] = -1                                    # skipped
+    slots[6] = N + 7                                 # out of range: skipped
+    pool = torch.full((N, 576), 0xAB, dtype=torch.uint8, device=DEV)
+    smla.fp8_pack_rows(torch.from_numpy(src).to(DEV), torch.from_numpy(slots).to(DEV), pool)
+    got = _np(pool)
+    ok = (slots >= 0) & (slots < N)
+    assert np.array_equal(got[slots[ok]], oracle.fp8_pack_rows_ref(src[ok]))
+    untouched = np.setdiff1d(np.arange(N), slots[ok])
+    assert np.all(got[untouched] == 0xAB)
+
+
+@pytest.mark.parametrize("T,H,N,K,empty_frac,splits", [
+    (7, 16, 6000, 1000, 0.1, 0),
+    (7, 16, 6000, 1000, 0.1, 1),
+    (7, 16, 6000, 1000, 0.1, 40),
+    (7, 16, 6000, 1000, 0.1, 1000),   # one tile per workgroup
+    (5, 32, 5000, 777, 0.2, 0),
+    (3, 64, 4000, 2048, 0.05, 0),
+    (2, 128, 3000, 300, 0.3, 5),
+    (9, 16, 2000, 1, 0.0, 0),         # a single entry per token
+    (4, 48, 2500, 130, 0.0, 3),       # 16-head blocks
+])
+def test_fp8pool_decode_matches_oracle(smla, T, H, N, K, empty_frac, splits):
+    _say("fp8pool decode", T, H, N, K, empty_frac, splits)
+    wl = W.custom(T=T, H=H, pool_rows=N, topk=K, empty_frac=empty_frac, seed=90 + K + splits)
+    src = W.pool_source(wl)
+    q = W.queries(wl)
+    idx = W.index_lists(wl)
+    rng = np.random.default_rng(K)
+    idx[rng.random(idx.shape) < 0.02] = N + 11      # out of range: empty
+    ref_idx = idx.copy()
+    ref_idx[ref_idx >= N] = -1
+    pool = build_device_fp8_pool(src, DEV)
+    out, lse = smla.sparse_mla_decode_fp8pool(torch.from_numpy(q).to(DEV), pool, torch.from_numpy(idx).to(DEV),
+                                              wl.softmax_scale, num_splits=splits)
+    ref_o, ref_l = oracle.sparse_mla_decode_fp8pool_ref(q, OracleFp8Rows(src), ref_idx, wl.softmax_scale)
+    assert_parity(_np(out), _np(lse), ref_o, ref_l, f"fp8pool T{T} H{H} K{K} splits{splits}")
+
+
+def test_fp8pool_empty_tokens(smla):
+    wl = W.custom(T=6, H=16, pool_rows=1000, topk=200, empty_frac=0.0, seed=97)
+    src, q, idx = W.pool_source(wl), W.queries(wl), W.index_lists(wl)
+    idx[2] = -1
+    idx[5, :] = 1000                                 # all out of range
+    ref_idx = idx.copy()
+    ref_idx[ref_idx >= 1000] = -1
+    pool = build_device_fp8_pool(src, DEV)
+    out, lse = smla.sparse_mla_decode_fp8pool(torch.from_numpy(q).to(DEV), pool, torch.from_numpy(idx).to(DEV),
+                                              wl.softmax_scale)
+    ref_o, ref_l = oracle.sparse_mla_decode_fp8pool_ref(q, OracleFp8Rows(src), ref_idx, wl.softmax_scale)
+    assert_parity(_np(out), _np(lse), ref_o, ref_l, "fp8pool empties")
+    assert np.all(_np(out)[[2, 5]] == 0) and np.all(np.isneginf(_np(lse)[[2, 5]]))
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_fp8pool_full_size(smla, cfg):
+    wl = W.WORKLOADS[cfg]
+    _say(f"fp8pool config {cfg} {wl.name}: T={wl.T} H={wl.H} pool={wl.pool_rows}")
+    src = pool_source_all(wl)
+    pool = build_device_fp8_pool(src, DEV)
+    q, idx = W.queries(wl), W.index_lists(wl)
+    out, lse = smla.sparse_mla_decode_fp8pool(torch.from_numpy(q).to(DEV), pool, torch.from_numpy(idx).to(DEV),
+                                              wl.softmax_scale)
+    out, lse = _np(out), _np(lse)
+    rng = np.random.default_rng(100 + cfg)
+    sample = rng.choice(wl.pool_rows, size=2048, replace=False)
+    got = _np(pool[torch.from_numpy(sample).to(DEV)])
+    assert np.array_equal(got, oracle.fp8_pack_rows_ref(src[sample]))
+    toks = sorted({0, wl.T - 1} | set(rng.choice(wl.T, size=4, replace=False).tolist()))
+    ref_o, ref_l = oracle.sparse_mla_decode_fp8pool_ref(q, OracleFp8Rows(src), idx, wl.softmax_scale, tokens=toks)
+    oe, le = assert_parity(out[toks], lse[toks], ref_o, ref_l, f"fp8pool config {cfg}")
+    assert np.all(np.isfinite(out))
+    _say(f"fp8pool config {cfg}: tokens {toks} out_err {oe:.2e} lse_err {le:.2e}")
