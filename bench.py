@@ -19,8 +19,9 @@ whole step; `roofline` prices the decode kernel's gathered KV bytes (352 bytes
 per valid list entry) against its average launch duration measured with HIP
 events around each launch on the launch stream; `cpu_baseline` times the CPU
 oracle on the host on the same workload.  Untimed for `value`, side legs report
-the staged two-pass variant, session-grouped decode and (`fp8_pool`) the same
-decode over the pool kept as 576-byte FP8 rows, the format NVFP4 replaces.
+the staged two-pass variant, session-grouped decode, (`fp8_pool`) the same
+decode over the pool kept as 576-byte FP8 rows, the format NVFP4 replaces, and
+(`indexer_topk`) the sparse indexer's top-2,048 selection that produces the lists.
 """
 
 import argparse
@@ -279,6 +280,53 @@ def fp8pool_timing(binding, wl, q, q_d, idx, idx_d, src_full, n_valid, fused_ms,
     return res
 
 
+def indexer_timing(binding, wl, steps, check_tokens):
+    """The sparse indexer's top-k selection (the step that produces the index lists) over
+    synthetic scores of each token's context, timed with events on the launch stream over
+    score copies spanning >= 2 GiB (each layer has scores of its own).  Algorithmic bytes:
+    the scores read once plus the lists written."""
+    import torch
+    import oracle
+    from sparse_mla_decode_04_amd import workloads as W
+    try:
+        scores, lengths, off = W.indexer_inputs(wl)
+    except ValueError:
+        return None
+    sc0 = torch.from_numpy(scores).to("cuda")
+    L = max(2, -(-COLD_SPAN_BYTES // (sc0.numel() * 4)))
+    copies = [sc0] + [sc0.clone() for _ in range(L - 1)]
+    len_d = torch.from_numpy(lengths).to("cuda")
+    off_d = torch.from_numpy(off).to("cuda")
+    out = torch.empty((wl.T, wl.topk), dtype=torch.int32, device="cuda")
+    for i in range(3):
+        binding.sparse_indexer_topk(copies[i % L], wl.topk, len_d, off_d, out)
+    torch.cuda.synchronize()
+    res = {"scores_per_token": int(scores.shape[1]), "score_copies": L}
+    if check_tokens > 0:
+        rng = np.random.default_rng(3)
+        toks = sorted(rng.choice(wl.T, size=min(wl.T, check_tokens), replace=False).tolist())
+        ref = oracle.topk_indices_ref(scores[toks], lengths[toks], wl.topk, off[toks])
+        if not np.array_equal(out.cpu().numpy()[toks], ref):
+            print("bench.py: indexer top-k does not match the oracle", file=sys.stderr)
+            sys.exit(3)
+        res["parity"] = {"tokens": toks, "bit_exact": True}
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        binding.sparse_indexer_topk(copies[(3 + i) % L], wl.topk, len_d, off_d, out)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    nbytes = scores.size * 4 + wl.T * wl.topk * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res.update({"us_per_launch": us, "steps": steps, "bytes": nbytes, "GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS})
+    log(f"indexer top-{wl.topk} over {scores.shape[1]} scores x {wl.T} tokens: {us:.1f} us per launch, "
+        f"{gbs:.0f} GB/s on {nbytes / 1e6:.1f} MB ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+    del copies, sc0, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(nbytes=256 << 20, reps=5):
     """A copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch of this copy,
     against its 256 MiB read and 256 MiB written, give the factors that turn those counters
@@ -310,6 +358,9 @@ def main():
     ap.add_argument("--fp8pool", type=int, default=50,
                     help="also time decode over the same pool kept as 576-byte FP8 rows for this many "
                          "steps (0 disables)")
+    ap.add_argument("--indexer", type=int, default=50,
+                    help="also time the sparse indexer's top-k selection over synthetic scores for this many "
+                         "steps, on workloads whose tokens have a context range (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -421,6 +472,8 @@ def main():
     fp8pool = (fp8pool_timing(binding, wl, q, q_d, idx, idx_d, src_full, n_valid, k_avg, args.fp8pool,
                               args.check_tokens) if args.fp8pool > 0 else None)
 
+    indexer = indexer_timing(binding, wl, args.indexer, args.check_tokens) if args.indexer > 0 else None
+
     traffic = traffic_from_profiles(wl.name)
     flops = 2.0 * wl.H * (576 + 512) * n_valid        # QK^T over 576 + PV over 512, per valid entry
     tflops = flops / (k_avg * 1e-3) / 1e12
@@ -459,6 +512,8 @@ def main():
         res["session_grouped"] = grouped
     if fp8pool:
         res["fp8_pool"] = fp8pool
+    if indexer:
+        res["indexer_topk"] = indexer
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(wl, q, idx, src_full, args.cpu_seconds)
         log(f"cpu oracle: {res['cpu_baseline']['value']:.1f} tokens/s")

@@ -201,6 +201,25 @@ SMLA_API int sparse_mla_decode_fp8pool(const void* q_dev, const void* fp8_pool_d
                                        void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * Sparse indexer, selection step ("Four-bit caches make room": the indexer picks the
+ * 2,048 context positions per decode token whose rows the decode kernel loads; the page
+ * gives no internals of its scoring, so the scores are an input here).
+ *   scores_dev      float32 [T][ld]: token t's scores at positions 0 .. lengths[t] - 1
+ *                   (the rest of the row is not read).  Not NaN.
+ *   lengths_dev     int32 [T], each clamped to [0, ld]; NULL = every token has ld positions
+ *   row_offset_dev  int32 [T]; NULL = 0
+ *   out_dev         int32 [T][k]: the k positions with the largest scores, equal scores
+ *                   (-0 equals +0) going to the lower position, as row_offset[t] + position
+ *                   in ascending position order; a token with fewer than k positions lists
+ *                   them all, then -1.  Entries must fit int32.
+ * 1 <= k <= 65536; ld >= 0 a multiple of 4, below 2^31; scores_dev 16-byte aligned (may be
+ * NULL when ld == 0).  One workgroup per token.
+ */
+SMLA_API int sparse_indexer_topk(const float* scores_dev, int64_t ld, const int32_t* lengths_dev,
+                                 const int32_t* row_offset_dev, int32_t T, int32_t k, int32_t* out_dev,
+                                 void* stream);
+
+/*
  * Grouped decode, step 1: union lists of token groups.  "Prime Intellect Launches Prime
  * Inference, Serving 600B Tokens Daily" (sections on the agent workload and on the
  * four-bit caches): the decode tokens of one agent session select largely the same cache

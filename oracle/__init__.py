@@ -32,6 +32,8 @@ Modules:
                pool of 576-byte FP8 rows.
   grouping  -- union lists of token groups and decode over them (the tokens of
                one agent session sharing most of their rows).
+  indexer   -- the sparse indexer's top-k selection over given scores (the step
+               that produces the index lists).
 
 Every function is pinned by tests under tests/ (test_oracle_*.py) against
 values that do not come from the oracle itself: hand-typed format tables,
@@ -51,3 +53,4 @@ from .attention import (  # noqa: F401
     sparse_mla_decode_fp8pool_ref,
 )
 from .grouping import group_union_ref, sparse_mla_decode_grouped_ref  # noqa: F401
+from .indexer import topk_indices_ref  # noqa: F401

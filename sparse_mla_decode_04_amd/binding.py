@@ -40,6 +40,7 @@ _SIGS = {
     "fp8_pack_rows": ([_P, _P, _I32, _P, _I64, _P], ctypes.c_int),
     "sparse_mla_decode_fp8pool": ([_P, _P, _I64, _P, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P],
                                   ctypes.c_int),
+    "sparse_indexer_topk": ([_P, _I64, _P, _P, _I32, _I32, _P, _P], ctypes.c_int),
     "smla_group_union": ([_P, _I32, _I32, _I32, _I64, _I32, _P, _P, _P], ctypes.c_int),
     "sparse_mla_decode_grouped": ([_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P],
                                   ctypes.c_int),
@@ -267,6 +268,23 @@ def prepare_pack(src, slots, kv_pool):
             _check(st, "nvfp4_pack_rows")
     call.tensors = keep
     return call
+
+
+# ---------------------------------------------------------------- sparse indexer ---
+
+def sparse_indexer_topk(scores, k, lengths=None, row_offset=None, out=None):
+    """Top-k selection over scores float32 [T, S] (S a multiple of 4): int32 [T, k] lists of
+    row_offset[t] + position, ascending, -1 past a token's length."""
+    if scores.dim() != 2:
+        raise ValueError("scores must be float32 [T, S]")
+    T, S = scores.shape
+    if out is None:
+        out = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    p_len = _dev(lengths, "lengths", torch.int32, (T,)) if lengths is not None else None
+    p_off = _dev(row_offset, "row_offset", torch.int32, (T,)) if row_offset is not None else None
+    _check(lib().sparse_indexer_topk(_dev(scores, "scores", torch.float32), S, p_len, p_off, T, k,
+                                     _dev(out, "out", torch.int32, (T, k)), _stream()), "sparse_indexer_topk")
+    return out
 
 
 # ---------------------------------------------------------------- grouped decode ---

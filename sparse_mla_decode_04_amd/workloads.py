@@ -29,7 +29,7 @@ TOPK = 2048             # entries per index list
 CHUNK_ROWS = 8192       # pool rows per independently seeded chunk
 
 # stream ids under a workload seed
-_S_POOL, _S_Q, _S_OFFSETS, _S_INDICES, _S_EMPTIES, _S_NEWROWS, _S_SLOTS = range(7)
+_S_POOL, _S_Q, _S_OFFSETS, _S_INDICES, _S_EMPTIES, _S_NEWROWS, _S_SLOTS, _S_SCORES = range(8)
 
 
 @dataclass(frozen=True)
@@ -171,6 +171,29 @@ def index_lists(wl):
     else:
         raise ValueError(wl.kind)
     return idx.astype(np.int32)
+
+
+def indexer_inputs(wl):
+    """Synthetic sparse-indexer inputs over each token's context: (scores float32 [T, S],
+    lengths int32 [T], row_offset int32 [T]).  The context is the pool range the token's
+    index list is drawn from (same offsets as index_lists; S = the context length).
+    Scores are N(0,1) on a grid of 1/64, so many positions tie at the top-2,048 cut.
+    Defined for the workloads whose tokens have a context range."""
+    T, N, p = wl.T, wl.pool_rows, wl.params
+    go = _rng(wl, _S_OFFSETS)
+    if wl.kind == "ranged":
+        offs = [int(go.integers(0, N - p["context"] + 1)) for _ in range(T)]
+    elif wl.kind == "sessions":
+        tps = p["tokens_per_session"]
+        offs = np.repeat([int(go.integers(0, N - p["context"] + 1)) for _ in range(p["sessions"])], tps)
+    else:
+        raise ValueError(f"no context ranges in workload {wl.name}")
+    S = p["context"]
+    g = _rng(wl, _S_SCORES)
+    scores = np.empty((T, S), dtype=np.float32)
+    for t in range(T):
+        scores[t] = np.round(g.standard_normal(S) * 64.0) / 64.0
+    return scores, np.full(T, S, dtype=np.int32), np.asarray(offs, dtype=np.int32)
 
 
 def new_rows(wl):

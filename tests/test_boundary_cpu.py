@@ -133,3 +133,14 @@ def test_fp8pool_entry_points_check_arguments(L):
     assert dec(pool_rows=8_000_000) == -2
     assert L.sparse_mla_decode(P(16), P(16), 8_000_000, P(16), 2, 16, 64, 0.1, P(16), P(16), 0,
                                None, 0, None) == -3
+
+
+def test_indexer_entry_point_checks_arguments(L):
+    assert L.sparse_indexer_topk(None, 8, None, None, 0, 4, None, None) == 0           # T == 0: no-op
+    assert L.sparse_indexer_topk(P(16), 8, None, None, 2, 0, P(16), None) == -1        # k < 1
+    assert L.sparse_indexer_topk(P(16), 8, None, None, 2, 65537, P(16), None) == -1    # k too large
+    assert L.sparse_indexer_topk(P(16), 6, None, None, 2, 4, P(16), None) == -1        # ld not a multiple of 4
+    assert L.sparse_indexer_topk(P(8), 8, None, None, 2, 4, P(16), None) == -1         # misaligned scores
+    assert L.sparse_indexer_topk(None, 8, None, None, 2, 4, P(16), None) == -1
+    assert L.sparse_indexer_topk(P(16), 8, P(2), None, 2, 4, P(16), None) == -1        # misaligned lengths
+    assert L.sparse_indexer_topk(P(16), 8, None, None, 2, 4, None, None) == -1         # no output
