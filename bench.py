@@ -123,6 +123,13 @@ def cpu_baseline(wl, q, idx, src, seconds):
                       f"BLAS with {blas} threads"}
 
 
+def backlog(torch, ms=20.0):
+    """Queue a spin kernel of about `ms` on the current stream, so that the launches and
+    events the host enqueues behind it run back to back (the side legs' Python calls take
+    longer to enqueue than some of their kernels take to run)."""
+    torch.cuda._sleep(int(ms * 2.0e6))
+
+
 def staged_timing(binding, wl, layers, q_d, idx_d, out, lse, ws, fused_ms, steps):
     """The staged two-pass variant the pages compare against: pass 1 writes every listed
     row as FP8 E4M3 to a [T][topk][576] buffer in HBM, pass 2 attends over it.  Timed with
@@ -145,6 +152,7 @@ def staged_timing(binding, wl, layers, q_d, idx_d, out, lse, ws, fused_ms, steps
         run(i)
     torch.cuda.synchronize()
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    backlog(torch)
     for i in range(steps):
         run(2 + i, evs[i])
     torch.cuda.synchronize()
@@ -211,6 +219,7 @@ def grouped_timing(binding, wl, layers, q, q_d, idx, idx_d, src_full, kv_bytes, 
             sys.exit(3)
         res["parity"] = {"tokens": toks, "out_err": oe, "lse_err": le}
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    backlog(torch)
     for i in range(steps):
         run(3 + i, evs[i])
     torch.cuda.synchronize()
@@ -264,6 +273,7 @@ def fp8pool_timing(binding, wl, q, q_d, idx, idx_d, src_full, n_valid, fused_ms,
             sys.exit(3)
         res["parity"] = {"tokens": toks, "out_err": oe, "lse_err": le}
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(steps)]
+    backlog(torch)
     for i in range(steps):
         evs[i][0].record()
         run(3 + i)
@@ -311,6 +321,7 @@ def indexer_timing(binding, wl, steps, check_tokens):
             sys.exit(3)
         res["parity"] = {"tokens": toks, "bit_exact": True}
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(steps)]
+    backlog(torch)
     for i in range(steps):
         evs[i][0].record()
         binding.sparse_indexer_topk(copies[(3 + i) % L], wl.topk, len_d, off_d, out)

@@ -11,36 +11,55 @@
 //   * entries are row_offset[t] + position, in ascending position order; a token with fewer
 //     than k positions lists them all, then -1.
 //
-// One workgroup of 1,024 threads per token.  Scores map to 32-bit keys whose unsigned order
-// is the numbers' order.  A radix select finds the k-th largest key K in three passes over
-// the token's scores (11, 11 and 10 key bits; each pass histograms, in LDS, the keys that
-// share the bits chosen so far, and a prefix sum over the bins from the top picks the bin
-// that holds the k-th key).  A last pass writes, in position order, every key above K and
-// the first `need` keys equal to K, placing each by a workgroup prefix sum of the counts.
-// The first pass reads the scores from HBM; the later ones mostly hit L2 / the Infinity
-// Cache (a 140,000-position token is 560 KB).
+// One workgroup of 512 threads per token.  Scores map to 32-bit keys whose unsigned order
+// is the numbers' order; the k-th largest key K is found by a radix select over 11, 11 and
+// 10 key bits (each step histograms, in LDS, the keys that share the bits chosen so far; a
+// prefix sum over the bins from the top picks the bin holding the k-th key).
+//   pass 1 (HBM): histogram of the top 11 bits of every key -> the bin b of the k-th key.
+//   pass 2 (L2):  keys above bin b are in the list: their positions are set in an LDS
+//                 bitmap; keys in bin b go to LDS with their positions (with N(0,1)-like
+//                 scores a few thousand).
+//   in LDS:       the two remaining radix steps over bin b's keys give K and how many keys
+//                 equal to K the list takes (`need`, lowest positions first); bin b's keys
+//                 above K join the bitmap, those equal to K go to a second one; popcount
+//                 prefix sums over the bitmap words then write the list in position order.
+// A context longer than the bitmaps, or a cut bin with more keys than LDS keeps (for
+// instance nearly equal scores), takes the remaining radix steps and the ordered write
+// from the scores in memory instead.
 #include <hip/hip_runtime.h>
 
 #include "smla.h"
 
 namespace {
 
-constexpr int kThreadsK = 1024;
+constexpr int kThreadsK = 512;
 constexpr int kWavesK = kThreadsK / 64;
 constexpr int kBins = 2048;
 constexpr int kMaxK = 65536;
+constexpr int kVec = 4;                         // 16-byte loads per thread per round
+constexpr int kRound = 4 * kVec * kThreadsK;    // positions per round
+constexpr int kCap = 4096;                      // keys of the cut bin kept in LDS
+constexpr int kCapWave = kCap / (kThreadsK / 64);   // each wave fills a region of its own
+constexpr int kMapWords = 4608;                 // position bitmap words: contexts up to 147,456
+static_assert(kBins % kThreadsK == 0, "every thread holds the same number of bins");
 
 struct SmemTopk {
   uint32_t hist[kBins];
+  uint32_t above[kMapWords];   // bit p: position p is in the list for certain (key above K)
+  uint32_t tie[kMapWords];     // bit p: key of position p equals K
+  uint32_t ckey[kCap];         // keys of the cut bin: wave w's in [w kCapWave, (w + 1) kCapWave)
+  int32_t cpos[kCap];          // their positions
   uint32_t wsum[kWavesK];
-  uint32_t pick[2];   // chosen bin, keys above it
+  uint32_t wcut[kWavesK];      // keys of the cut bin each wave found
+  uint32_t pick[2];            // chosen bin, keys above it
 };
 
-// Unsigned order of the key = numeric order of the score; -0 maps to the key of +0.
+// Unsigned order of the key = numeric order of the score; -0 maps to the key of +0 (adding
+// +0 turns -0 into +0 and leaves every other value, subnormals included, as it is).  No
+// compares: a negative score's bits are inverted, a positive one's sign bit is set.
 __device__ __forceinline__ uint32_t score_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u << 1) == 0u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // Inclusive prefix sum of v over the workgroup's threads in thread order; `total` gets the
@@ -67,22 +86,186 @@ __device__ __forceinline__ uint32_t block_scan(SmemTopk& sm, uint32_t v, uint32_
   return x + before;
 }
 
-// Keys of positions p0 .. p0 + 3 (those below n); `in` marks which exist.
-__device__ __forceinline__ void load_keys(const float* __restrict__ s, int64_t p0, int64_t n, uint32_t (&key)[4],
-                                          bool (&in)[4]) {
-  if (p0 + 3 < n) {
-    const float4 v = *(const float4*)(s + p0);
+// Keys of positions p .. p + 3 (those below n) into key[0..3]; absent ones are not used.
+__device__ __forceinline__ void load4(const float* __restrict__ s, int64_t p, int64_t n, uint32_t* key) {
+  if (p + 3 < n) {
+    const float4 v = *(const float4*)(s + p);
     key[0] = score_key(v.x);
     key[1] = score_key(v.y);
     key[2] = score_key(v.z);
     key[3] = score_key(v.w);
-    in[0] = in[1] = in[2] = in[3] = true;
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      in[j] = p0 + j < n;
-      key[j] = in[j] ? score_key(s[p0 + j]) : 0u;
+    for (int j = 0; j < 4; j++) key[j] = p + j < n ? score_key(s[p + j]) : 0u;
+  }
+}
+
+// Keys of the 4 kVec positions a thread takes in a round: 16-byte loads at p + 4 j * stride
+// (j < kVec), all issued before any is used.  A full round (every position below n) loads
+// without tests, so nothing stands between the loads; the last round tests each position.
+template <bool kFull>
+__device__ __forceinline__ void load_round(const float* __restrict__ s, int64_t p, int64_t stride, int64_t n,
+                                           uint32_t (&key)[4 * kVec]) {
+  if constexpr (kFull) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    f4 v[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; j++) v[j] = *(const f4*)(s + p + 4 * j * stride);
+    __builtin_amdgcn_sched_barrier(0);   // every load is issued before any is used
+#pragma unroll
+    for (int j = 0; j < kVec; j++) {
+      key[4 * j + 0] = score_key(v[j].x);
+      key[4 * j + 1] = score_key(v[j].y);
+      key[4 * j + 2] = score_key(v[j].z);
+      key[4 * j + 3] = score_key(v[j].w);
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kVec; j++) load4(s, p + 4 * j * stride, n, key + 4 * j);
+  }
+}
+
+// Raw 16-byte loads of a full round (positions p + 4 j stride, j < kVec), issued together.
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void issue_round(const float* __restrict__ s, int64_t p, int64_t stride,
+                                            f4v (&v)[kVec]) {
+#pragma unroll
+  for (int j = 0; j < kVec; j++) v[j] = *(const f4v*)(s + p + 4 * j * stride);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void keys_of(const f4v (&v)[kVec], uint32_t (&key)[4 * kVec]) {
+#pragma unroll
+  for (int j = 0; j < kVec; j++) {
+    key[4 * j + 0] = score_key(v[j].x);
+    key[4 * j + 1] = score_key(v[j].y);
+    key[4 * j + 2] = score_key(v[j].z);
+    key[4 * j + 3] = score_key(v[j].w);
+  }
+}
+
+// g(key[], c, full) for every round of the token: thread tid takes the 16-byte pieces tid,
+// tid + kThreadsK, ... of each round (every load instruction of a wave reads 1 KB of
+// consecutive scores).  Two register buffers: the loads of round r + 1 are in flight while
+// round r is processed.  The last, partial round tests each position.
+template <class G>
+__device__ __forceinline__ void for_rounds(const float* __restrict__ s, int64_t n, G g) {
+  const int tid = threadIdx.x;
+  const int64_t rounds = n / kRound;
+  const int64_t p = 4 * tid;
+  f4v a[kVec], b[kVec];
+  uint32_t key[4 * kVec];
+  if (rounds > 0) issue_round(s, p, kThreadsK, a);
+  for (int64_t r = 0; r < rounds; r += 2) {
+    if (r + 1 < rounds) issue_round(s, (r + 1) * kRound + p, kThreadsK, b);
+    keys_of(a, key);
+    g(key, r * kRound, true);
+    if (r + 1 >= rounds) break;
+    if (r + 2 < rounds) issue_round(s, (r + 2) * kRound + p, kThreadsK, a);
+    keys_of(b, key);
+    g(key, (r + 1) * kRound, true);
+  }
+  const int64_t c = rounds * kRound;
+  if (c < n) {
+    load_round<false>(s, c + p, kThreadsK, n, key);
+    g(key, c, false);
+  }
+}
+
+// f(key, position) for every key of the token (not in position order).
+template <class F>
+__device__ __forceinline__ void for_keys_global(const float* __restrict__ s, int64_t n, F f) {
+  const int tid = threadIdx.x;
+  for_rounds(s, n, [&](const uint32_t (&key)[4 * kVec], int64_t c, bool full) {
+#pragma unroll
+    for (int j = 0; j < kVec; j++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int64_t q = c + 4 * (tid + (int64_t)kThreadsK * j) + e;
+        if (full || q < n) f(key[4 * j + e], q);
+      }
+  });
+}
+
+// One radix step: histogram of bits (shift .. shift + log2(bmask + 1)) of the keys that
+// match `prefix` under `pmask`, then the bin of the need-th largest; narrows prefix / pmask
+// and takes the keys of higher bins off `need`.  `visit(f)` calls f(key) for every key.
+template <class V>
+__device__ __forceinline__ void radix_step(SmemTopk& sm, V visit, int shift, uint32_t bmask, uint32_t& prefix,
+                                           uint32_t& pmask, uint32_t& need) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBins; i += kThreadsK) sm.hist[i] = 0;
+  __syncthreads();
+  const uint32_t pf = prefix, pm = pmask;
+  visit([&](uint32_t key, int64_t) {
+    if ((key & pm) == pf) atomicAdd(&sm.hist[(key >> shift) & bmask], 1u);
+  });
+  __syncthreads();
+  // thread tid holds the kPerBins bins of descending rank kPerBins tid .. + kPerBins - 1
+  constexpr int kPerBins = kBins / kThreadsK;
+  uint32_t h[kPerBins], sum = 0;
+#pragma unroll
+  for (int i = 0; i < kPerBins; i++) {
+    const int b = (int)bmask - kPerBins * tid - i;
+    h[i] = b >= 0 ? sm.hist[b] : 0u;
+    sum += h[i];
+  }
+  uint32_t tot;
+  uint32_t before = block_scan(sm, sum, tot) - sum;   // keys in higher bins
+#pragma unroll
+  for (int i = 0; i < kPerBins; i++) {
+    if (before < need && need <= before + h[i]) {   // true for exactly one bin of the workgroup
+      sm.pick[0] = (uint32_t)((int)bmask - kPerBins * tid - i);
+      sm.pick[1] = before;
+    }
+    before += h[i];
+  }
+  __syncthreads();
+  prefix |= sm.pick[0] << shift;
+  pmask |= bmask << shift;
+  need -= sm.pick[1];
+  __syncthreads();
+}
+
+// The list from `cnt` (key, position) pairs in position order, given by at(i, key, pos):
+// every key above K and the first `need` keys equal to K.  gb / eb count the keys above K /
+// equal to K before a pair; its place is gb + min(eb, need).  The places are below k by
+// construction; the test only keeps a write inside the token's row.
+template <class A>
+__device__ __forceinline__ void emit(SmemTopk& sm, int64_t cnt, A at, uint32_t K, uint32_t need, int32_t off,
+                                     int32_t* __restrict__ o, int32_t k) {
+  const int tid = threadIdx.x;
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int64_t c = 0; c < cnt; c += 4 * kThreadsK) {
+    const int64_t i0 = c + 4 * tid;
+    uint32_t key[4];
+    int32_t pos[4];
+    at(i0, key, pos);
+    uint32_t g = 0, e = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      g += (i0 + j < cnt && key[j] > K) ? 1u : 0u;
+      e += (i0 + j < cnt && key[j] == K) ? 1u : 0u;
+    }
+    const uint32_t mine = g | (e << 16);   // at most 4 kThreadsK of each per chunk
+    uint32_t tot;
+    const uint32_t excl = block_scan(sm, mine, tot) - mine;
+    uint32_t gb = gt_run + (excl & 0xFFFFu), eb = eq_run + (excl >> 16);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if (i0 + j >= cnt) continue;
+      const int32_t entry = off + pos[j];
+      if (key[j] > K) {
+        const uint32_t place = gb + (eb < need ? eb : need);
+        if (place < (uint32_t)k) o[place] = entry;
+        gb++;
+      } else if (key[j] == K) {
+        if (eb < need && gb + eb < (uint32_t)k) o[gb + eb] = entry;
+        eb++;
+      }
+    }
+    gt_run += tot & 0xFFFFu;
+    eq_run += tot >> 16;
   }
 }
 
@@ -102,79 +285,148 @@ __global__ __launch_bounds__(kThreadsK) void sparse_indexer_topk_kernel(const fl
     for (int p = tid; p < k; p += kThreadsK) o[p] = p < n ? off + p : -1;
     return;
   }
+  auto global_keys = [&](auto f) { for_keys_global(s, n, f); };
 
-  // ---- radix select: after the passes, prefix = K (the k-th largest key) and `need` keys
-  // equal to K belong to the list (the count of keys equal to K is at least need >= 1)
+  // ---- pass 1: the top-11-bit bin of the k-th key
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)k;
-  for (int pass = 0; pass < 3; pass++) {
-    const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
-    const uint32_t bmask = pass == 2 ? 1023u : 2047u;
-    for (int i = tid; i < kBins; i += kThreadsK) sm.hist[i] = 0;
-    __syncthreads();
-    for (int64_t p0 = 4 * tid; p0 < n; p0 += 4 * kThreadsK) {
-      uint32_t key[4];
-      bool in[4];
-      load_keys(s, p0, n, key, in);
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        if (in[j] && (key[j] & pmask) == prefix) atomicAdd(&sm.hist[(key[j] >> shift) & bmask], 1u);
-    }
-    __syncthreads();
-    // thread tid holds the bins of descending rank 2 tid and 2 tid + 1
-    const int b0 = (int)bmask - 2 * tid, b1 = b0 - 1;
-    const uint32_t h0 = b0 >= 0 ? sm.hist[b0] : 0u, h1 = b1 >= 0 ? sm.hist[b1] : 0u;
-    uint32_t tot;
-    const uint32_t before = block_scan(sm, h0 + h1, tot) - h0 - h1;   // keys in higher bins
-    if (before < need && need <= before + h0) {
-      sm.pick[0] = (uint32_t)b0;
-      sm.pick[1] = before;
-    } else if (before + h0 < need && need <= before + h0 + h1) {
-      sm.pick[0] = (uint32_t)b1;
-      sm.pick[1] = before + h0;
-    }
-    __syncthreads();
-    prefix |= sm.pick[0] << shift;
-    pmask |= bmask << shift;
-    need -= sm.pick[1];
-    __syncthreads();
-  }
-  const uint32_t K = prefix;
+  radix_step(sm, global_keys, 21, 2047u, prefix, pmask, need);
 
-  // ---- write the list in position order: keys above K, and the first `need` keys equal to
-  // K.  gb / eb: keys above K / equal to K at lower positions; an entry goes to gb +
-  // min(eb, need).
-  uint32_t gt_run = 0, eq_run = 0;
-  for (int64_t c = 0; c < n; c += 4 * kThreadsK) {
-    const int64_t p0 = c + 4 * tid;
-    uint32_t key[4];
-    bool in[4];
-    load_keys(s, p0, n, key, in);
-    uint32_t g = 0, e = 0;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      g += (in[j] && key[j] > K) ? 1u : 0u;
-      e += (in[j] && key[j] == K) ? 1u : 0u;
+  const int64_t W = (n + 31) >> 5;   // bitmap words of the context
+  uint32_t cut = prefix >> 21;        // the chosen top-11-bit bin
+  // opaque to the optimizer, which would otherwise turn the sign-bit tests below back into
+  // compare-and-select pairs
+  asm volatile("" : "+v"(cut));
+  uint32_t cnt = kCap + 1;
+  if (W <= kMapWords) {
+    // ---- pass 2: keys above the cut bin are in the list: set their bits; keys in the cut
+    // bin go to LDS with their positions
+    for (int64_t i = tid; i < W; i += kThreadsK) {
+      sm.above[i] = 0;
+      sm.tie[i] = 0;
     }
-    const uint32_t mine = g | (e << 16);   // at most 4,096 of each per chunk
-    uint32_t tot;
-    const uint32_t excl = block_scan(sm, mine, tot) - mine;
-    uint32_t gb = gt_run + (excl & 0xFFFFu), eb = eq_run + (excl >> 16);
+    __syncthreads();
+    const int wave = tid >> 6;
+    uint32_t wfill = 0;   // keys of the cut bin this wave found so far (uniform in the wave)
+    // one round.  The 4 positions of a 16-byte load share one bitmap word (they start at a
+    // multiple of 4), so each load sets its bits with one OR (of 0 when none is above the
+    // cut).  A lane's cut-bin keys go to its wave's region after those of lower lanes: the
+    // wave prefix sum of the counts (below 32) is built from ballots of their five bits.
+    auto round = [&](const uint32_t (&key)[4 * kVec], int64_t c, bool full) {
+      uint32_t cutm[kVec], m = 0;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      if (!in[j]) continue;
-      const int32_t entry = off + (int32_t)(p0 + j);
-      // the places are below k by construction; the test only keeps a write inside the row
-      if (key[j] > K) {
-        const uint32_t at = gb + (eb < need ? eb : need);
-        if (at < (uint32_t)k) o[at] = entry;
-        gb++;
-      } else if (key[j] == K) {
-        if (eb < need && gb + eb < (uint32_t)k) o[gb + eb] = entry;
-        eb++;
+      for (int j = 0; j < kVec; j++) {
+        const int64_t p = c + 4 * (tid + (int64_t)kThreadsK * j);
+        uint32_t am = 0, cm = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          // bins are below 2^11: cut - b is negative exactly when b > cut, and
+          // (b ^ cut) - 1 exactly when b == cut
+          const uint32_t b = key[4 * j + e] >> 21;
+          uint32_t above = (cut - b) >> 31, equal = ((b ^ cut) - 1u) >> 31;
+          if (!full && p + e >= n) above = equal = 0;
+          am |= above << e;
+          cm |= equal << e;
+        }
+        if (p < n) atomicOr(&sm.above[p >> 5], am << (p & 31));
+        cutm[j] = cm;
+        m += __builtin_popcount(cm);
+      }
+      uint32_t before = 0, total = 0;
+#pragma unroll
+      for (int bit = 0; bit < 5; bit++) {
+        const uint64_t bal = __ballot((m >> bit) & 1u);
+        before += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))
+                  << bit;
+        total += (uint32_t)__popcll(bal) << bit;
+      }
+      if (m != 0) {
+        uint32_t i = wfill + before;
+#pragma unroll
+        for (int j = 0; j < kVec; j++) {
+          if (cutm[j] == 0) continue;
+          const int64_t p = c + 4 * (tid + (int64_t)kThreadsK * j);
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            if ((cutm[j] >> e) & 1u) {
+              if (i < (uint32_t)kCapWave) {
+                sm.ckey[wave * kCapWave + i] = key[4 * j + e];
+                sm.cpos[wave * kCapWave + i] = (int32_t)(p + e);
+              }
+              i++;
+            }
+          }
+        }
+      }
+      wfill += total;
+    };
+    for_rounds(s, n, round);
+    if ((tid & 63) == 0) sm.wcut[wave] = wfill;
+    __syncthreads();
+    cnt = 0;
+    for (int w = 0; w < kWavesK; w++) cnt = sm.wcut[w] > (uint32_t)kCapWave ? (uint32_t)kCap + 1 : cnt + sm.wcut[w];
+  }
+
+  if (cnt <= (uint32_t)kCap) {
+    // ---- the two remaining radix steps over the cut bin's keys, in LDS
+    // entry i of the buffer holds a key when it lies below its wave's fill
+    auto kept = [&](int i) { return (uint32_t)(i % kCapWave) < sm.wcut[i / kCapWave]; };
+    auto lds_keys = [&](auto f) {
+      for (int i = tid; i < kCap; i += kThreadsK)
+        if (kept(i)) f(sm.ckey[i], (int64_t)0);
+    };
+    radix_step(sm, lds_keys, 10, 2047u, prefix, pmask, need);
+    radix_step(sm, lds_keys, 0, 1023u, prefix, pmask, need);
+    const uint32_t K = prefix;
+    for (int i = tid; i < kCap; i += kThreadsK) {
+      if (!kept(i)) continue;
+      const uint32_t key = sm.ckey[i];
+      const int32_t p = sm.cpos[i];
+      if (key > K) atomicOr(&sm.above[p >> 5], 1u << (p & 31));
+      else if (key == K) atomicOr(&sm.tie[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+    // ---- the list from the bitmaps: thread tid takes words [w0, w1); a set bit of `above`
+    // goes to gb + min(eb, need), one of `tie` to gb + eb while eb < need (gb / eb: bits of
+    // `above` / `tie` at lower positions)
+    const int per = (int)((W + kThreadsK - 1) / kThreadsK);
+    const int w0 = tid * per, w1 = (int)(w0 + per < W ? w0 + per : W);
+    uint32_t g = 0, e = 0;
+    for (int w = w0; w < w1; w++) {
+      g += __builtin_popcount(sm.above[w]);
+      e += __builtin_popcount(sm.tie[w]);
+    }
+    uint32_t tot;
+    uint32_t gb = block_scan(sm, g, tot) - g;
+    uint32_t eb = block_scan(sm, e, tot) - e;
+    for (int w = w0; w < w1; w++) {
+      const uint32_t a = sm.above[w], t = sm.tie[w];
+      uint32_t m = a | t;
+      while (m) {
+        const int bit = __builtin_ctz(m);
+        m &= m - 1;
+        const int32_t entry = off + (w * 32 + bit);
+        // the places are below k by construction; the test only keeps a write inside the row
+        if ((a >> bit) & 1u) {
+          const uint32_t place = gb + (eb < need ? eb : need);
+          if (place < (uint32_t)k) o[place] = entry;
+          gb++;
+        } else {
+          if (eb < need && gb + eb < (uint32_t)k) o[gb + eb] = entry;
+          eb++;
+        }
       }
     }
-    gt_run += tot & 0xFFFFu;
-    eq_run += tot >> 16;
+  } else {
+    // ---- a long context or a crowded cut bin: the rest from the scores in memory
+    radix_step(sm, global_keys, 10, 2047u, prefix, pmask, need);
+    radix_step(sm, global_keys, 0, 1023u, prefix, pmask, need);
+    emit(sm, n,
+         [&](int64_t i0, uint32_t* key, int32_t* pos) {
+           load4(s, i0, n, key);
+#pragma unroll
+           for (int j = 0; j < 4; j++) pos[j] = (int32_t)(i0 + j);
+         },
+         prefix, need, off, o, k);
   }
 }
 

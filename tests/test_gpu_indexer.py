@@ -106,3 +106,28 @@ def test_indexer_lists_drive_decode(smla):
     toks = [0, 11, 34]
     ref_o, ref_l = oracle.sparse_mla_decode_ref(q, OracleRows(src), ref_idx, wl.softmax_scale, tokens=toks)
     assert_parity(out.cpu().numpy()[toks], lse.cpu().numpy()[toks], ref_o, ref_l, "indexer -> decode")
+
+
+@pytest.mark.parametrize("kind", ["equal", "grid"])
+def test_topk_crowded_cut_bin(smla, kind):
+    """Far more keys share the cut's top 11 bits than LDS keeps (all equal, or three
+    values): the selection finishes from the scores in memory."""
+    rng = np.random.default_rng(21)
+    T, S = 4, 60000
+    scores = _scores(kind, T, S, rng) if kind == "equal" else rng.integers(0, 3, size=(T, S)).astype(np.float32)
+    lengths = np.array([S, 50001, 40000, 2049], dtype=np.int32)
+    for k in (2048, 100):
+        got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), k, torch.from_numpy(lengths).to(DEV))
+        assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, k))
+
+
+def test_topk_context_longer_than_the_bitmaps(smla):
+    """Contexts of more than 147,456 positions take the path that reads the scores again."""
+    rng = np.random.default_rng(31)
+    T, S = 4, 300000
+    scores = (np.round(rng.standard_normal((T, S)) * 64) / 64).astype(np.float32)
+    lengths = np.array([S, 147457, 147456, 147455], dtype=np.int32)
+    off = np.array([5, 0, 1000000, 7], dtype=np.int32)
+    got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), 2048, torch.from_numpy(lengths).to(DEV),
+                                   torch.from_numpy(off).to(DEV))
+    assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, 2048, off))
