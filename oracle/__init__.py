@@ -34,6 +34,8 @@ Modules:
                one agent session sharing most of their rows).
   indexer   -- the sparse indexer's top-k selection over given scores (the step
                that produces the index lists).
+  layout    -- the block-major multi-layer pool layout (blocks of every layer kept
+               together).
 
 Every function is pinned by tests under tests/ (test_oracle_*.py) against
 values that do not come from the oracle itself: hand-typed format tables,
@@ -54,3 +56,4 @@ from .attention import (  # noqa: F401
 )
 from .grouping import group_union_ref, sparse_mla_decode_grouped_ref  # noqa: F401
 from .indexer import topk_indices_ref  # noqa: F401
+from .layout import blocked_pool_ref, layer_rows_ref, storage_row_ref  # noqa: F401
