@@ -21,7 +21,9 @@ events around each launch on the launch stream; `cpu_baseline` times the CPU
 oracle on the host on the same workload.  Untimed for `value`, side legs report
 the staged two-pass variant, session-grouped decode, (`fp8_pool`) the same
 decode over the pool kept as 576-byte FP8 rows, the format NVFP4 replaces, and
-(`indexer_topk`) the sparse indexer's top-2,048 selection that produces the lists.
+(`indexer_topk`) the sparse indexer's top-2,048 selection that produces the lists,
+and (`block_major_pool`) decode and block transfer over the block-major multi-layer
+cache layout.
 """
 
 import argparse
@@ -338,6 +340,115 @@ def indexer_timing(binding, wl, steps, check_tokens):
     return res
 
 
+def blhnc_timing(binding, wl, q, q_d, idx, idx_d, src_full, layers, kv_bytes, fused_ms, steps, check_tokens,
+                 block_rows=16, context_rows=146000):
+    """The block-major multi-layer cache (one block of every layer stored together):
+      * decode: the pool's layers in one [blocks][layers][block_rows][352] allocation
+        spanning >= 2 GiB, each layer written by nvfp4_pack_rows_blhnc from the fp16 source
+        rows, sparse_mla_decode_blhnc of a different layer each launch, against the
+        layer-major launch;
+      * transfer: one request's blocks (a context of 146,000 rows as seeded scattered
+        blocks) gathered into a contiguous send buffer with blhnc_copy_blocks, one segment
+        per block, against the layer-major cache, one segment per block and layer (one call
+        per layer tensor).  Bytes = what is read plus what is written."""
+    import torch
+    import oracle
+    from helpers import OracleRows, parity_errors
+    N, B = wl.pool_rows, block_rows
+    if N % B:
+        return None
+    nb = N // B
+    layer_bytes = N * ROW_BYTES
+    L = max(2, -(-COLD_SPAN_BYTES // layer_bytes))
+    if L * layer_bytes > 0xFFFFF000:
+        return None
+    pool = torch.empty((nb, L, B, ROW_BYTES), dtype=torch.uint8, device="cuda")
+    src_d = torch.from_numpy(src_full).to("cuda")
+    slots = torch.arange(N, dtype=torch.int32, device="cuda")
+    for l in range(L):
+        binding.nvfp4_pack_rows_blhnc(src_d, slots, pool, l)
+    del src_d, slots
+    out = torch.empty((wl.T, wl.H, 512), dtype=torch.float16, device="cuda")
+    lse = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
+    ws = binding.make_workspace(wl.T, wl.H, wl.topk, 0, "cuda")
+
+    def run(i):
+        binding.sparse_mla_decode_blhnc(q_d, pool, i % L, idx_d, wl.softmax_scale, out, lse, 0, ws)
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    res = {"layers": L, "block_rows": B, "allocation_bytes": int(pool.numel())}
+    if check_tokens > 0:
+        rng = np.random.default_rng(4)
+        toks = sorted(rng.choice(wl.T, size=min(wl.T, check_tokens), replace=False).tolist())
+        ref_o, ref_l = oracle.sparse_mla_decode_ref(q, OracleRows(src_full), idx, wl.softmax_scale, tokens=toks)
+        oe, le, ok = parity_errors(out.cpu().numpy()[toks], lse.cpu().numpy()[toks], ref_o, ref_l)
+        log(f"block-major decode parity on tokens {toks}: out err {oe:.2e}, lse err {le:.2e}, -inf ok {ok}")
+        if not (oe <= 2e-3 and le <= 1e-3 and ok):
+            print("bench.py: block-major decode does not match the oracle", file=sys.stderr)
+            sys.exit(3)
+        res["parity"] = {"tokens": toks, "out_err": oe, "lse_err": le}
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(steps)]
+    backlog(torch)
+    for i in range(steps):
+        evs[i][0].record()
+        run(3 + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    res.update({"decode_us_per_launch": us, "steps": steps, "gathered_kv_GBs": kv_bytes / (us * 1e-6) / 1e9,
+                "layer_major_us": fused_ms * 1e3})
+    log(f"block-major pool ({L} layers, {B}-row blocks, {pool.numel() / 1e9:.2f} GB): decode {us:.1f} us per "
+        f"launch vs layer-major {fused_ms * 1e3:.1f} us")
+
+    # transfer of one request's blocks
+    nblk = min(nb, -(-context_rows // B))
+    rng = np.random.default_rng(5)
+    ids_h = rng.permutation(nb)[:nblk].astype(np.int32)
+    ids = torch.from_numpy(ids_h).to("cuda")
+    send = torch.empty((nblk, L, B, ROW_BYTES), dtype=torch.uint8, device="cuda")
+    lm = [p.view(nb, B, ROW_BYTES) for p in layers[:L]] if len(layers) >= L else None
+    send_lm = torch.empty((L, nblk, B, ROW_BYTES), dtype=torch.uint8, device="cuda")
+
+    def xfer_blocked():
+        binding.blhnc_copy_blocks(pool, send, src_ids=ids)
+
+    def xfer_layer_major():
+        for l in range(L):
+            binding.blhnc_copy_blocks(lm[l], send_lm[l], src_ids=ids)
+
+    xfer_blocked()
+    torch.cuda.synchronize()
+    if not torch.equal(send[:, L - 1], pool[ids.long(), L - 1]):
+        print("bench.py: block transfer does not match its source blocks", file=sys.stderr)
+        sys.exit(3)
+    moved = 2 * nblk * L * B * ROW_BYTES
+    tr = {"blocks": nblk, "bytes_moved": moved, "segments_block_major": nblk, "segments_layer_major": nblk * L}
+    for name, fn in (("block_major", xfer_blocked), ("layer_major", xfer_layer_major if lm else None)):
+        if fn is None:
+            continue
+        fn()
+        ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(20)]
+        backlog(torch)
+        for i in range(20):
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        tr[name + "_us"] = t
+        tr[name + "_GBs"] = moved / (t * 1e-6) / 1e9
+    res["transfer"] = tr
+    log(f"transfer of {nblk} blocks ({moved / 2e6:.1f} MB): block-major {tr['block_major_us']:.1f} us "
+        f"({tr['block_major_GBs']:.0f} GB/s, {nblk} segments)" +
+        (f", layer-major {tr['layer_major_us']:.1f} us ({tr['layer_major_GBs']:.0f} GB/s, {nblk * L} segments "
+         f"in {L} calls)" if "layer_major_us" in tr else ""))
+    del pool, send, send_lm, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(nbytes=256 << 20, reps=5):
     """A copy of known size: rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch of this copy,
     against its 256 MiB read and 256 MiB written, give the factors that turn those counters
@@ -372,6 +483,9 @@ def main():
     ap.add_argument("--indexer", type=int, default=50,
                     help="also time the sparse indexer's top-k selection over synthetic scores for this many "
                          "steps, on workloads whose tokens have a context range (0 disables)")
+    ap.add_argument("--blhnc", type=int, default=50,
+                    help="launches of the block-major multi-layer pool decode leg, with its block transfer "
+                         "(0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
     args = ap.parse_args()
@@ -485,6 +599,9 @@ def main():
 
     indexer = indexer_timing(binding, wl, args.indexer, args.check_tokens) if args.indexer > 0 else None
 
+    blhnc = (blhnc_timing(binding, wl, q, q_d, idx, idx_d, src_full, layers, kv_bytes, k_avg, args.blhnc,
+                          args.check_tokens) if args.blhnc > 0 else None)
+
     traffic = traffic_from_profiles(wl.name)
     flops = 2.0 * wl.H * (576 + 512) * n_valid        # QK^T over 576 + PV over 512, per valid entry
     tflops = flops / (k_avg * 1e-3) / 1e12
@@ -525,6 +642,8 @@ def main():
         res["fp8_pool"] = fp8pool
     if indexer:
         res["indexer_topk"] = indexer
+    if blhnc:
+        res["block_major_pool"] = blhnc
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(wl, q, idx, src_full, args.cpu_seconds)
         log(f"cpu oracle: {res['cpu_baseline']['value']:.1f} tokens/s")

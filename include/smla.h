@@ -265,6 +265,63 @@ SMLA_API int sparse_mla_decode_grouped(const void* q_dev, const void* kv_pool_de
 SMLA_API size_t smla_decode_grouped_workspace_bytes(int32_t T, int32_t H, int32_t tpg, int32_t U,
                                                     int32_t num_splits);
 
+/*
+ * Block-major multi-layer cache ("Prime Intellect Launches Prime Inference, Serving 600B
+ * Tokens Daily", section on the BLHNC layout: the data of several layers is stored together
+ * for each block, so that one block of every layer is one contiguous piece and moving a
+ * request's cache needs one transfer per block rather than one per block and layer).
+ * The layout (a cache row has no head axis, so within a block a layer's rows follow one
+ * another):
+ *   pool_dev  uint8 [pool_blocks][layers][block_rows][352]
+ *   row v of layer l is allocation row ((v / block_rows) * layers + l) * block_rows
+ *   + v % block_rows.  Each layer has pool_blocks * block_rows rows.
+ * block_rows is a power of two, 1 .. 65536; layers >= 1 with layers * block_rows < 2^24;
+ * 0 <= layer < layers.  A malformed layout returns SMLA_ERR_INVALID_ARG.
+ */
+
+/*
+ * Cache write of layer `layer` into a block-major pool: nvfp4_pack_rows with slots_dev
+ * naming rows of that layer (0 .. pool_blocks * block_rows - 1; negative or past the end =
+ * skipped, slots distinct).  The row bytes are those nvfp4_pack_rows writes.
+ * pool_blocks * block_rows must fit int32 (SMLA_ERR_UNSUPPORTED otherwise).
+ */
+SMLA_API int nvfp4_pack_rows_blhnc(const void* src_dev, const int32_t* slots_dev, int32_t n,
+                                   void* pool_dev, int64_t pool_blocks, int32_t layers, int32_t layer,
+                                   int32_t block_rows, void* stream);
+
+/*
+ * Sparse MLA decode of layer `layer` of a block-major pool: indices_dev names rows of that
+ * layer (negative or >= pool_blocks * block_rows = empty), and every other argument, the
+ * result and the workspace rule are those of sparse_mla_decode (smla_decode_workspace_bytes
+ * gives the size).  The result equals sparse_mla_decode over the layer's rows laid out one
+ * after another.  The whole allocation, pool_blocks * layers * block_rows * 352 bytes, must
+ * stay within 0xFFFFF000 bytes (about 12.2 million rows over all layers), else
+ * SMLA_ERR_UNSUPPORTED.
+ */
+SMLA_API int sparse_mla_decode_blhnc(const void* q_dev, const void* pool_dev, int64_t pool_blocks,
+                                     int32_t layers, int32_t layer, int32_t block_rows,
+                                     const int32_t* indices_dev, int32_t T, int32_t H, int32_t topk,
+                                     float softmax_scale, void* out_dev, float* lse_dev, int32_t num_splits,
+                                     void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * Block transfer: copies n segments of block_bytes bytes, segment src_ids_dev[i] of src_dev
+ * (src_blocks segments) to segment dst_ids_dev[i] of dst_dev (dst_blocks segments).  With
+ * block_bytes = layers * block_rows * 352 a segment is one block of a block-major pool, every
+ * layer; gathering a request's blocks into a contiguous send buffer passes dst_ids_dev =
+ * NULL (segment i), scattering a received buffer into free blocks passes src_ids_dev = NULL.
+ * The copy of a layer-major cache is the same call with block_bytes = block_rows * 352 and
+ * one segment per block and layer.
+ *   A pair whose source or destination id is negative or past its array is skipped.
+ *   Destination segments must not overlap each other or any source segment.
+ *   block_bytes > 0, a multiple of 16 and below 2^36; the pointers 16-byte aligned, id
+ *   arrays 4-byte aligned; n * ceil(block_bytes / 16384) < 2^24 (SMLA_ERR_UNSUPPORTED
+ *   otherwise).  Device memory on both sides; n == 0 enqueues nothing.
+ */
+SMLA_API int blhnc_copy_blocks(const void* src_dev, int64_t src_blocks, const int32_t* src_ids_dev,
+                               void* dst_dev, int64_t dst_blocks, const int32_t* dst_ids_dev, int32_t n,
+                               int64_t block_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ Modules:
   indexer   -- the sparse indexer's top-k selection over given scores (the step
                that produces the index lists).
   layout    -- the block-major multi-layer pool layout (blocks of every layer kept
-               together).
+               together), block transfers, and decode of one layer of such a pool.
 
 Every function is pinned by tests under tests/ (test_oracle_*.py) against
 values that do not come from the oracle itself: hand-typed format tables,
@@ -56,4 +56,6 @@ from .attention import (  # noqa: F401
 )
 from .grouping import group_union_ref, sparse_mla_decode_grouped_ref  # noqa: F401
 from .indexer import topk_indices_ref  # noqa: F401
-from .layout import blocked_pool_ref, layer_rows_ref, storage_row_ref  # noqa: F401
+from .layout import (  # noqa: F401
+    blocked_pool_ref, layer_rows_ref, storage_row_ref, copy_blocks_ref, sparse_mla_decode_blhnc_ref,
+)

@@ -45,6 +45,10 @@ _SIGS = {
     "sparse_mla_decode_grouped": ([_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P],
                                   ctypes.c_int),
     "smla_decode_grouped_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
+    "nvfp4_pack_rows_blhnc": ([_P, _P, _I32, _P, _I64, _I32, _I32, _I32, _P], ctypes.c_int),
+    "sparse_mla_decode_blhnc": ([_P, _P, _I64, _I32, _I32, _I32, _P, _I32, _I32, _I32, _F32, _P, _P, _I32, _P,
+                                 _SZ, _P], ctypes.c_int),
+    "blhnc_copy_blocks": ([_P, _I64, _P, _P, _I64, _P, _I32, _I64, _P], ctypes.c_int),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -152,6 +156,9 @@ def _decode_common(entry, q, rows, pool_rows, indices, softmax_scale, out, lse, 
             _dev(lse, "lse", torch.float32, (T, H)), int(num_splits), p_ws, workspace.numel(), _stream())
     if entry == "sparse_mla_decode":
         st = lib().sparse_mla_decode(p_q, rows, pool_rows, p_idx, *tail)
+    elif entry == "sparse_mla_decode_blhnc":
+        nb, layers, layer, B = pool_rows   # the block-major layout
+        st = lib().sparse_mla_decode_blhnc(p_q, rows, nb, layers, layer, B, p_idx, *tail)
     elif entry == "sparse_mla_decode_fp8pool":
         st = lib().sparse_mla_decode_fp8pool(p_q, rows, pool_rows, p_idx, *tail)
     else:
@@ -341,3 +348,53 @@ def sparse_mla_decode_grouped(q, kv_pool, union, tpg, softmax_scale, out=None, l
         "sparse_mla_decode_grouped")
     return out, lse
 
+
+
+def _blhnc_pool(pool):
+    if pool.dim() != 4 or pool.shape[3] != ROW_BYTES:
+        raise ValueError("pool must be uint8 [blocks, layers, block_rows, 352]")
+    return _dev(pool, "pool", torch.uint8), int(pool.shape[0]), int(pool.shape[1]), int(pool.shape[2])
+
+
+def nvfp4_pack_rows_blhnc(src, slots, pool, layer):
+    """Quantize fp16 rows src[n, 576] into rows slots[n] of layer `layer` of a block-major
+    pool uint8 [blocks, layers, block_rows, 352]."""
+    n = src.shape[0] if src.dim() == 2 else -1
+    p_src = _dev(src, "src", torch.float16, (n, HEAD_DIM))
+    p_slots = _dev(slots, "slots", torch.int32, (n,))
+    p_pool, nb, layers, B = _blhnc_pool(pool)
+    _check(lib().nvfp4_pack_rows_blhnc(p_src, p_slots, n, p_pool, nb, layers, int(layer), B, _stream()),
+           "nvfp4_pack_rows_blhnc")
+
+
+def sparse_mla_decode_blhnc(q, pool, layer, indices, softmax_scale, out=None, lse=None, num_splits=0,
+                            workspace=None):
+    """Sparse MLA decode of layer `layer` of a block-major pool uint8 [blocks, layers,
+    block_rows, 352]: returns (out fp16 [T, H, 512], lse fp32 [T, H])."""
+    p_pool, nb, layers, B = _blhnc_pool(pool)
+    return _decode_common("sparse_mla_decode_blhnc", q, p_pool, (nb, layers, int(layer), B), indices,
+                          softmax_scale, out, lse, num_splits, workspace)
+
+
+def blhnc_copy_blocks(src, dst, src_ids=None, dst_ids=None, n=None):
+    """Copy whole segments (the first dimension of src and dst, same segment size): segment
+    src_ids[i] of src to segment dst_ids[i] of dst (None = segment i)."""
+    if src.dim() < 1 or dst.dim() < 1:
+        raise ValueError("src and dst must have a segment dimension")
+    seg = src[0].numel() * src.element_size() if src.shape[0] else 0
+    dseg = dst[0].numel() * dst.element_size() if dst.shape[0] else 0
+    if src.shape[0] and dst.shape[0] and seg != dseg:
+        raise ValueError("src and dst segments differ in size")
+    seg = seg or dseg
+    if n is None:
+        n = (src_ids if src_ids is not None else dst_ids if dst_ids is not None else src).shape[0]
+    p_src = _dev(src, "src", src.dtype)
+    p_dst = _dev(dst, "dst", dst.dtype)
+    p_sid = _dev(src_ids, "src_ids", torch.int32) if src_ids is not None else None
+    p_did = _dev(dst_ids, "dst_ids", torch.int32) if dst_ids is not None else None
+    for ids, name in ((src_ids, "src_ids"), (dst_ids, "dst_ids")):
+        if ids is not None and (ids.dim() != 1 or ids.shape[0] < n):
+            raise ValueError(f"{name} must be int32 [n]")
+    _check(lib().blhnc_copy_blocks(p_src, src.shape[0], p_sid, p_dst, dst.shape[0], p_did, int(n), seg,
+                                   _stream()), "blhnc_copy_blocks")
+    return dst

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsmla.so")
-SOURCES = ["codec.hip", "decode.hip", "decode_regs.hip", "decode_ws.hip", "group.hip", "indexer.hip", "api.hip"]
+SOURCES = ["codec.hip", "decode.hip", "decode_regs.hip", "decode_ws.hip", "group.hip", "indexer.hip", "layout.hip", "api.hip"]
 # per-source flags: the 64-head kernel keeps its 128-value accumulator in the MFMA
 # accumulation registers, so it is built without the VGPR-only MFMA form
 NO_VGPR_FORM = {"decode_ws.hip"}

@@ -103,7 +103,7 @@ enum class Rows { kNvfp4Pool, kFp8Staged, kFp8Pool };
 int run_decode(Rows kind, const void* q, const void* rows, int64_t pool_rows,
                const int32_t* idx, int32_t T, int32_t H, int32_t topk, float softmax_scale,
                void* out, float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream,
-               int32_t tok_heads = 0) {
+               int32_t tok_heads = 0, const RowMap& map = identity_rowmap(), uint64_t alloc_rows = 0) {
   const bool grouped = tok_heads > 0;
   const bool fp8rows = kind != Rows::kNvfp4Pool;
   int st = check_decode(q, rows, pool_rows, idx, T, H, topk, softmax_scale, out, lse, num_splits);
@@ -111,8 +111,10 @@ int run_decode(Rows kind, const void* q, const void* rows, int64_t pool_rows,
   // every buffer the kernels address through a buffer resource must fit its byte range
   const uint64_t idx_bytes = (uint64_t)T * topk * 4;
   const uint64_t q_bytes = (uint64_t)T * H * 576 * 2;
+  // (a block-major pool's allocation holds alloc_rows rows, every layer's)
   const uint64_t rows_bytes = kind == Rows::kFp8Staged ? (uint64_t)T * topk * 576
-                              : (uint64_t)pool_rows * (kind == Rows::kFp8Pool ? 576 : 352);
+                              : alloc_rows > 0     ? alloc_rows * 352
+                                                   : (uint64_t)pool_rows * (kind == Rows::kFp8Pool ? 576 : 352);
   if (idx_bytes > kMaxBufferBytes || rows_bytes > kMaxBufferBytes || q_bytes > kMaxBufferBytes)
     return SMLA_ERR_UNSUPPORTED;
   if ((int64_t)T * ((topk + kTileRows - 1) / kTileRows) >= (int64_t)1 << 31) return SMLA_ERR_UNSUPPORTED;
@@ -145,10 +147,26 @@ int run_decode(Rows kind, const void* q, const void* rows, int64_t pool_rows,
   a.part_lse_bytes = (uint32_t)(p.counters_off - p.part_lse_off);
   a.tok_heads = tok_heads;
   a.fp8_pool = kind == Rows::kFp8Pool;
+  a.map = map;
   const hipError_t e = grouped ? launch_decode_grouped(a, (hipStream_t)stream)
                        : fp8rows ? launch_decode_fp8rows(a, (hipStream_t)stream)
                                  : launch_decode_nvfp4(a, (hipStream_t)stream, decode_variant());
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+// Block-major multi-layer pool [pool_blocks][layers][block_rows][352]: the map of layer
+// `layer`'s rows, or false for a malformed layout.  Block sizes are powers of two.
+bool blhnc_map(int64_t pool_blocks, int32_t layers, int32_t layer, int32_t block_rows, RowMap& m) {
+  if (pool_blocks < 0 || layers < 1 || layer < 0 || layer >= layers || block_rows < 1 ||
+      block_rows > (1 << 16) || (block_rows & (block_rows - 1)) != 0)
+    return false;
+  uint32_t shift = 0;
+  while ((1 << shift) < block_rows) shift++;
+  m.shift = shift;
+  m.mask = (uint32_t)block_rows - 1u;
+  m.stride = (uint32_t)((int64_t)layers * block_rows);
+  m.layer = (uint32_t)((int64_t)layer * block_rows);
+  return (int64_t)layers * block_rows < (1 << 24);
 }
 
 // Grouped decode shapes: tpg tokens of H heads per group make the 64 heads of one block.
@@ -178,8 +196,42 @@ SMLA_API int nvfp4_pack_rows(const void* src, const int32_t* slots, int32_t n, v
   if (n == 0) return SMLA_OK;
   if (!src || !slots || !pool || !aligned16(src) || !aligned4(slots) || !aligned16(pool))
     return SMLA_ERR_INVALID_ARG;
-  return launch_pack(src, slots, n, pool, pool_rows, (hipStream_t)stream) == hipSuccess ? SMLA_OK
-                                                                                        : SMLA_ERR_LAUNCH;
+  return launch_pack(src, slots, n, pool, pool_rows, identity_rowmap(), (hipStream_t)stream) == hipSuccess
+             ? SMLA_OK
+             : SMLA_ERR_LAUNCH;
+}
+
+SMLA_API int nvfp4_pack_rows_blhnc(const void* src, const int32_t* slots, int32_t n, void* pool,
+                                   int64_t pool_blocks, int32_t layers, int32_t layer, int32_t block_rows,
+                                   void* stream) {
+  RowMap m;
+  if (n < 0 || !blhnc_map(pool_blocks, layers, layer, block_rows, m)) return SMLA_ERR_INVALID_ARG;
+  if (n == 0) return SMLA_OK;
+  if (!src || !slots || !pool || !aligned16(src) || !aligned4(slots) || !aligned16(pool))
+    return SMLA_ERR_INVALID_ARG;
+  if (pool_blocks > ((int64_t)1 << 31) / block_rows) return SMLA_ERR_UNSUPPORTED;   // slots are int32
+  return launch_pack(src, slots, n, pool, pool_blocks * block_rows, m, (hipStream_t)stream) == hipSuccess
+             ? SMLA_OK
+             : SMLA_ERR_LAUNCH;
+}
+
+SMLA_API int blhnc_copy_blocks(const void* src, int64_t src_blocks, const int32_t* src_ids, void* dst,
+                               int64_t dst_blocks, const int32_t* dst_ids, int32_t n, int64_t block_bytes,
+                               void* stream) {
+  if (n < 0 || src_blocks < 0 || dst_blocks < 0 || block_bytes <= 0 || block_bytes % 16 != 0)
+    return SMLA_ERR_INVALID_ARG;
+  if (n == 0) return SMLA_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst) || (src_ids && !aligned4(src_ids)) ||
+      (dst_ids && !aligned4(dst_ids)))
+    return SMLA_ERR_INVALID_ARG;
+  // segment ids are int32; the grid holds fewer than 2^24 workgroups of 256 lanes
+  const uint64_t chunks = ((uint64_t)block_bytes / 16 + 1023) / 1024;
+  if (block_bytes >= ((int64_t)1 << 36) || (uint64_t)n * chunks >= ((uint64_t)1 << 24))
+    return SMLA_ERR_UNSUPPORTED;
+  return launch_copy_segments(src, src_blocks, src_ids, dst, dst_blocks, dst_ids, n, block_bytes,
+                              (hipStream_t)stream) == hipSuccess
+             ? SMLA_OK
+             : SMLA_ERR_LAUNCH;
 }
 
 SMLA_API int nvfp4_unpack_rows_f16(const void* pool, int64_t pool_rows, const int32_t* rows, int32_t n,
@@ -211,6 +263,18 @@ SMLA_API int sparse_mla_decode(const void* q, const void* pool, int64_t pool_row
                       float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
   return run_decode(Rows::kNvfp4Pool, q, pool, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
                     num_splits, ws, ws_bytes, stream);
+}
+
+SMLA_API int sparse_mla_decode_blhnc(const void* q, const void* pool, int64_t pool_blocks, int32_t layers,
+                                     int32_t layer, int32_t block_rows, const int32_t* idx, int32_t T,
+                                     int32_t H, int32_t topk, float softmax_scale, void* out, float* lse,
+                                     int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
+  RowMap m;
+  if (!blhnc_map(pool_blocks, layers, layer, block_rows, m)) return SMLA_ERR_INVALID_ARG;
+  const uint64_t alloc_rows = (uint64_t)pool_blocks * (uint64_t)layers * (uint64_t)block_rows;
+  if (alloc_rows * 352 > kMaxBufferBytes) return SMLA_ERR_UNSUPPORTED;
+  return run_decode(Rows::kNvfp4Pool, q, pool, pool_blocks * block_rows, idx, T, H, topk, softmax_scale,
+                    out, lse, num_splits, ws, ws_bytes, stream, 0, m, alloc_rows);
 }
 
 SMLA_API int sparse_mla_combine(const float* part_o, const float* part_lse, int32_t T, int32_t S, int32_t H,

@@ -12,11 +12,12 @@ namespace smla {
 
 // One wave per row.  Lanes 0..31 own latent group g = lane (16 values), lanes 32..63 own
 // rope values 2r, 2r+1 (r = lane - 32).  The 352-byte row is assembled in LDS and written
-// with 22 coalesced 16-byte stores.
+// with 22 coalesced 16-byte stores, at the allocation row `map` gives for the slot (the
+// slot itself in a layer-major pool).
 __global__ __launch_bounds__(256) void nvfp4_pack_rows_kernel(const f16* __restrict__ src,
                                                                const int32_t* __restrict__ slots,
                                                                int32_t n, uint8_t* __restrict__ pool,
-                                                               int64_t pool_rows) {
+                                                               int64_t pool_rows, RowMap map) {
   __shared__ __attribute__((aligned(16))) uint8_t rowbuf[4][kRowBytes];
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wid;
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(256) void nvfp4_pack_rows_kernel(const f16* __restr
   __syncthreads();
   if (active && lane < kRowBytes / 16) {
     const u32x4 v = lds_load<u32x4>(rb + 16 * lane);
-    *(u32x4*)(pool + (int64_t)slot * kRowBytes + 16 * lane) = v;
+    *(u32x4*)(pool + storage_row_wide((uint32_t)slot, map) * kRowBytes + 16 * lane) = v;
   }
 }
 
@@ -156,10 +157,10 @@ hipError_t launch_fp8_pack(const void* src, const int32_t* slots, int32_t n, voi
 }
 
 hipError_t launch_pack(const void* src, const int32_t* slots, int32_t n, void* pool,
-                       int64_t pool_rows, hipStream_t s) {
+                       int64_t pool_rows, const RowMap& map, hipStream_t s) {
   const int blocks = (n + 3) / 4;
   hipLaunchKernelGGL(nvfp4_pack_rows_kernel, dim3(blocks), dim3(256), 0, s, (const f16*)src, slots,
-                     n, (uint8_t*)pool, pool_rows);
+                     n, (uint8_t*)pool, pool_rows, map);
   return hipGetLastError();
 }
 

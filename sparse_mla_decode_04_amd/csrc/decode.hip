@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256, WPC) void sparse_mla_decode_kernel(DecodeArgs 
     if constexpr (kFp8)
       base = (uint32_t)(A.fp8_pool ? v : cur.t * A.topk + k) * (uint32_t)kHeadDim;
     else
-      base = (uint32_t)v * (uint32_t)kRowBytes;
+      base = storage_row((uint32_t)v, A.map) * (uint32_t)kRowBytes;
     const uint32_t lds0 = lds_addr(ring + (i % ST) * F::kSlot + wid * F::kPortion);
 #pragma unroll
     for (int kk = 0; kk < F::kLoads; kk++) {

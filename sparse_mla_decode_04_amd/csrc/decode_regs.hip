@@ -103,12 +103,12 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   // This lane's bytes of row v for tile cur (the code pieces at instruction offsets from one
   // lane base; a row outside the list, the range or the pool reads as zeros, scales
   // included, so an empty row scales its PV contribution by zero); returns the wave's
-  // valid-row mask.  Row ids are below 2^24 (the pool fits the buffer range), so the
-  // 24-bit multiply is exact.
+  // valid-row mask.  Allocation rows are below 2^24 (the pool fits the buffer range), so
+  // the 24-bit multiply is exact.
   const uint32_t lane_c = 64u * g, lane_s = (uint32_t)kScaleOff + 8u * g, lane_r = (uint32_t)kRopeOff + 16u * g;
   auto issue_rows = [&](const Cursor& cur, int32_t v, RowRegs& R) -> uint32_t {
     const bool ok = cur.c < c_hi && cur.ci * kTileRows + row < A.topk && row_valid(v, A.pool_rows);
-    const uint32_t vb = ok ? __umul24((uint32_t)v, (uint32_t)kRowBytes) : kOOB;
+    const uint32_t vb = ok ? __umul24(storage_row((uint32_t)v, A.map), (uint32_t)kRowBytes) : kOOB;
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) R.cw[kk] = ld128(rs_rows, vb + lane_c + 16u * kk);
     R.sc = ld64(rs_rows, vb + lane_s);
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   auto row_base = [&](const Cursor& cur, int32_t v, uint32_t& vmask) -> uint32_t {
     const bool ok = cur.c < c_hi && cur.ci * kTileRows + row < A.topk && row_valid(v, A.pool_rows);
     vmask = __builtin_amdgcn_readfirstlane((uint32_t)__ballot(ok && g == 0) & 0xFFFFu);
-    return ok ? __umul24((uint32_t)v, (uint32_t)kRowBytes) : kOOB;
+    return ok ? __umul24(storage_row((uint32_t)v, A.map), (uint32_t)kRowBytes) : kOOB;
   };
 
   f32x4 O[1][8];

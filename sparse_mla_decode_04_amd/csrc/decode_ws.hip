@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
       const int32_t v = kGrouped ? (e < 0 ? -1 : (e & kRowMask)) : e;
       const bool ok = cur.c < c_hi && k < A.topk && row_valid(v, A.pool_rows);
       if (kGrouped && g == 0) sm.members[i % kST][kWR * wid + r16] = ok ? (uint8_t)(e >> kMemberShift) : 0;
-      const uint32_t base = (uint32_t)v * (uint32_t)kRowBytes;
+      const uint32_t base = storage_row((uint32_t)v, A.map) * (uint32_t)kRowBytes;
       const uint32_t lds0 = lds_addr(ring + (i % kST) * kSlot + wid * kPortion);
 #pragma unroll
       for (int kk = 0; kk < kLoads; kk++) {

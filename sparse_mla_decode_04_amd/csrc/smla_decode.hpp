@@ -15,6 +15,7 @@
 // and applies it to all heads of its block.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -31,6 +32,27 @@ constexpr int kMemberShift = 27;
 constexpr int32_t kRowMask = (1 << kMemberShift) - 1;
 constexpr int kMaxGroupTokens = 4;
 constexpr int kMaxGroupEntries = 8192;   // tokens per group x topk the union builder takes
+
+// Where row v of a layer's list lives in the allocation the kernels read.  A layer-major
+// pool holds the layer's rows one after another (identity map).  A block-major
+// multi-layer pool ("Prime Intellect Launches Prime Inference, Serving 600B Tokens Daily",
+// section on the BLHNC layout: the data of several layers stored together for each block)
+// is [block][layer][row in block][row bytes], so row v of layer l sits at allocation row
+// ((v >> shift) * stride + layer) + (v & mask), with block size B = 1 << shift,
+// mask = B - 1, stride = layers * B and layer = l * B.
+struct RowMap {
+  uint32_t shift, mask, stride, layer;
+};
+__host__ __device__ inline RowMap identity_rowmap() { return RowMap{0u, 0u, 1u, 0u}; }
+// Every term stays below 2^24 (the host bounds the allocation by the buffer range, which
+// holds fewer than 2^24 rows), so the 24-bit multiply is exact.
+__device__ __forceinline__ uint32_t storage_row(uint32_t v, const RowMap& m) {
+  return __umul24(v >> m.shift, m.stride) + m.layer + (v & m.mask);
+}
+// The same for any non-negative row id, in 64 bits (writers, whose pools are not bounded).
+__host__ __device__ inline uint64_t storage_row_wide(uint32_t v, const RowMap& m) {
+  return (uint64_t)(v >> m.shift) * m.stride + m.layer + (v & m.mask);
+}
 
 struct DecodeArgs {
   const void* q;            // fp16 [T][H][576]
@@ -56,6 +78,7 @@ struct DecodeArgs {
   uint32_t part_o_bytes;    // bytes of part_o
   uint32_t part_lse_bytes;  // bytes of part_lse
   int32_t fp8_pool;         // FP8 rows: 1 = row v of a pool, 0 = the staged row of entry (t, j)
+  RowMap map;               // list row -> allocation row of a pool (identity unless block-major)
 };
 
 struct DecodePlan {

@@ -8,8 +8,9 @@
 
 namespace smla {
 
+// `map` places layer row `slot` in the allocation (identity for a layer-major pool).
 hipError_t launch_pack(const void* src, const int32_t* slots, int32_t n, void* pool,
-                       int64_t pool_rows, hipStream_t s);
+                       int64_t pool_rows, const RowMap& map, hipStream_t s);
 hipError_t launch_unpack(const void* pool, int64_t pool_rows, const int32_t* rows, int32_t n,
                          void* out, hipStream_t s);
 hipError_t launch_fp8_pack(const void* src, const int32_t* slots, int32_t n, void* pool, int64_t pool_rows,
@@ -30,6 +31,11 @@ hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_group_union(const int32_t* idx, int32_t T, int32_t topk, int32_t tpg, int64_t pool_rows,
                               int32_t U, int32_t* uni, int32_t* count, hipStream_t s);
 hipError_t launch_decode_fp8rows(const DecodeArgs& a, hipStream_t s);
+// Copies n segments of seg_bytes (a multiple of 16) from src segment src_ids[i] to dst
+// segment dst_ids[i] (layout.hip); a null id array means segment i.
+hipError_t launch_copy_segments(const void* src, int64_t src_segs, const int32_t* src_ids, void* dst,
+                                int64_t dst_segs, const int32_t* dst_ids, int32_t n, int64_t seg_bytes,
+                                hipStream_t s);
 hipError_t launch_combine(const float* part_o, const float* part_lse, int32_t T, int32_t S,
                           int32_t H, void* out, float* lse, hipStream_t s);
 

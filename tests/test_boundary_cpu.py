@@ -144,3 +144,31 @@ def test_indexer_entry_point_checks_arguments(L):
     assert L.sparse_indexer_topk(None, 8, None, None, 2, 4, P(16), None) == -1
     assert L.sparse_indexer_topk(P(16), 8, P(2), None, 2, 4, P(16), None) == -1        # misaligned lengths
     assert L.sparse_indexer_topk(P(16), 8, None, None, 2, 4, None, None) == -1         # no output
+
+
+def test_blhnc_entry_points_check_arguments(L):
+    def dec(nb=100, layers=4, layer=1, B=16, ws=None):
+        return L.sparse_mla_decode_blhnc(P(16), P(16), nb, layers, layer, B, P(16), 2, 16, 64, 0.1, P(16),
+                                         P(16), 0, ws, 0, None)
+    assert dec(B=12) == -1                               # block size not a power of two
+    assert dec(B=0) == -1
+    assert dec(layer=4) == -1                            # layer past the layers
+    assert dec(layer=-1) == -1
+    assert dec(layers=0) == -1
+    assert dec(nb=-1) == -1
+    assert dec(layers=1 << 10, B=1 << 14) == -1          # stride layers * B reaches 2^24
+    assert dec() == -3                                   # well formed: workspace missing
+    # the whole allocation (every layer) must fit one buffer resource's byte range
+    assert dec(nb=1_000_000 // 16 * 4, layers=4) == -2
+    assert L.nvfp4_pack_rows_blhnc(None, None, 0, None, 10, 2, 0, 8, None) == 0          # n == 0
+    assert L.nvfp4_pack_rows_blhnc(P(16), P(16), 3, P(16), 10, 2, 2, 8, None) == -1      # bad layer
+    assert L.nvfp4_pack_rows_blhnc(P(16), P(16), 3, P(8), 10, 2, 0, 8, None) == -1       # misaligned pool
+    assert L.nvfp4_pack_rows_blhnc(P(16), P(16), 3, P(16), 1 << 29, 2, 0, 8, None) == -2  # rows past int32
+    cp = L.blhnc_copy_blocks
+    assert cp(None, 0, None, None, 0, None, 0, 16, None) == 0                           # n == 0
+    assert cp(P(16), 4, None, P(16), 4, None, 2, 24, None) == -1                        # not a multiple of 16
+    assert cp(P(16), 4, None, P(16), 4, None, 2, 0, None) == -1
+    assert cp(P(8), 4, None, P(16), 4, None, 2, 16, None) == -1                         # misaligned source
+    assert cp(P(16), 4, P(2), P(16), 4, None, 2, 16, None) == -1                        # misaligned ids
+    assert cp(P(16), 4, None, None, 4, None, 2, 16, None) == -1
+    assert cp(P(16), 4, None, P(16), 4, None, 1 << 20, 1 << 20, None) == -2             # grid too large
