@@ -14,10 +14,15 @@ so a step never finds its rows in the 256 MB Infinity Cache left by the steps
 before it (as in serving, where the other layers run between two launches of one
 layer).
 
+The K timed steps run as one replay of a captured HIP graph (the way a serving
+loop launches decode; --graph 0 launches them one by one from the host), checked
+bit for bit against the eager launch.
+
 Prints one JSON line on stdout.  `value` is decode tokens per second of the
 whole step; `roofline` prices the decode kernel's gathered KV bytes (352 bytes
 per valid list entry) against its average launch duration measured with HIP
-events around each launch on the launch stream; `cpu_baseline` times the CPU
+events on the launch stream around a run of back-to-back launches queued behind a
+backlog (so the events bracket the kernels and not the host); `cpu_baseline` times the CPU
 oracle on the host on the same workload.  Untimed for `value`, side legs report
 the staged two-pass variant, session-grouped decode, (`fp8_pool`) the same
 decode over the pool kept as 576-byte FP8 rows, the format NVFP4 replaces, and
@@ -483,6 +488,9 @@ def main():
     ap.add_argument("--indexer", type=int, default=50,
                     help="also time the sparse indexer's top-k selection over synthetic scores for this many "
                          "steps, on workloads whose tokens have a context range (0 disables)")
+    ap.add_argument("--graph", type=int, default=1,
+                    help="1: time the K steps as one replay of a captured HIP graph (default); 0: K eager "
+                         "launches from the host")
     ap.add_argument("--blhnc", type=int, default=50,
                     help="launches of the block-major multi-layer pool decode leg, with its block transfer "
                          "(0 = skip)")
@@ -570,22 +578,70 @@ def main():
             print("bench.py: output does not match the oracle", file=sys.stderr)
             sys.exit(3)
 
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kms = np.array([a.elapsed_time(b) for a, b, _ in evs])
-    k_avg = float(np.mean(kms))
-    achieved = kv_bytes / (k_avg * 1e-3) / 1e9
-    log(f"decode launch: mean {k_avg * 1e3:.2f} us, median {np.median(kms) * 1e3:.2f} us, "
-        f"min {np.min(kms) * 1e3:.2f} us; step {ms_per_step * 1e3:.2f} us; "
-        f"gathered KV {kv_bytes / 1e6:.2f} MB -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+    if args.graph:
+        # The K timed steps as one HIP graph (captured, replayed once untimed, then timed):
+        # the host enqueues one replay instead of K launches.  Every step's output is the
+        # same (identical layer copies, the same rows written), so each replay must leave the
+        # eager result bit for bit.
+        ref_out, ref_lse = out.clone(), lse.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(args.warmup + i)
+        graph.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
+            print("bench.py: graph replay differs from the eager launch", file=sys.stderr)
+            sys.exit(3)
+        out.zero_()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
+            print("bench.py: graph replay differs from the eager launch", file=sys.stderr)
+            sys.exit(3)
+        del graph
+        # launch durations: a run of eager launches of one kernel queued behind a backlog, one
+        # HIP event before and one after the run on the launch stream
+        n_ev = min(args.steps, 200)
 
-    pack_us = float(np.mean([c.elapsed_time(a) for a, b, c in evs])) * 1e3 if pack else None
+        def bracket(fn):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            backlog(torch)
+            e0.record()
+            for i in range(n_ev):
+                fn(args.warmup + args.steps + i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n_ev
+
+        k_run = bracket(lambda i: decode[i % L]())
+        pack_run = bracket(lambda i: pack[i % L]()) if pack else None
+    else:
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    if args.graph:
+        k_avg = k_run
+        pack_us = pack_run * 1e3 if pack else None
+        log(f"decode launch: mean {k_avg * 1e3:.2f} us over {n_ev} back-to-back launches; "
+            f"step {ms_per_step * 1e3:.2f} us (graph replay)")
+    else:
+        kms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+        k_avg = float(np.mean(kms))
+        pack_us = float(np.mean([c.elapsed_time(a) for a, b, c in evs])) * 1e3 if pack else None
+        log(f"decode launch: mean {k_avg * 1e3:.2f} us, median {np.median(kms) * 1e3:.2f} us, "
+            f"min {np.min(kms) * 1e3:.2f} us; step {ms_per_step * 1e3:.2f} us")
+    achieved = kv_bytes / (k_avg * 1e-3) / 1e9
+    log(f"gathered KV {kv_bytes / 1e6:.2f} MB -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
     if pack:
         log(f"cache write ({len(slots)} rows): mean {pack_us:.2f} us")
     staged_steps = args.staged if args.staged >= 0 else (20 if pack else 0)
@@ -626,6 +682,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": wl.name, "decode_tokens": wl.T, "heads": wl.H, "topk": wl.topk,
+                   "launch": "hip_graph" if args.graph else "eager",
                    "pool_rows": wl.pool_rows, "valid_entries": n_valid, "row_bytes": ROW_BYTES,
                    "cache_write_rows": int(len(slots)), "layer_copies": L,
                    "num_splits": args.num_splits or smla.choose_num_splits(wl.T, wl.H, wl.topk),
