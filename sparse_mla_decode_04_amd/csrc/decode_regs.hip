@@ -245,16 +245,42 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   // then holds rows 8g..8g+7 and dword 1 rows 32+8g.. of feature 16*tau + r16.  An empty
   // tile has zero probabilities and scales, so it adds nothing.
   const int Rt = (r16 < 8) ? (8 * g + r16) : (32 + 8 * g + r16 - 8);
+  // The LDS reads of step k+2 are issued before the arithmetic of step k (the fences keep
+  // the compiler from sinking them to their use or hoisting the next step's unpack), so each
+  // step's reads have two steps of unpack and matrix work to land.
   auto pv = [&](int par, const f16x8 (&bop)[2]) {
     const SMLA_LDS uint8_t* tb = codes + par * kCodeSlot + (Rt >> 4) * kCodePortion + 16 * (Rt & 15);
+    auto rd = [&](int k, u32x2& d, f16x8& s0, f16x8& s1) {
+      const int tau = 8 * wid + k;
+      d = lds_read_tr4(tb + 256 * (tau >> 1) + 8 * (tau & 1));
+      s0 = lds_load<f16x8>(&sm.sc[par][tau][8 * g]);
+      s1 = lds_load<f16x8>(&sm.sc[par][tau][32 + 8 * g]);
+    };
+    u32x2 d0, d1;
+    f16x8 p0, p1, q0, q1;   // scales of step k (p) and k+1 (q)
+    rd(0, d0, p0, p1);
+    rd(1, d1, q0, q1);
 #pragma unroll
     for (int k = 0; k < 8; k++) {
-      const int tau = 8 * wid + k;
-      const u32x2 d = lds_read_tr4(tb + 256 * (tau >> 1) + 8 * (tau & 1));
-      const f16x8 sc0 = lds_load<f16x8>(&sm.sc[par][tau][8 * g]);
-      const f16x8 sc1 = lds_load<f16x8>(&sm.sc[par][tau][32 + 8 * g]);
-      O[0][k] = mfma16x16x32(unpack8_pairs(d.x, sc0), bop[0], O[0][k]);
-      O[0][k] = mfma16x16x32(unpack8_pairs(d.y, sc1), bop[1], O[0][k]);
+      u32x2 dn;
+      f16x8 n0, n1;
+      if (k < 6) rd(k + 2, dn, n0, n1);
+      asm volatile("" ::: "memory");
+      f16x8 a0 = unpack8_pairs(d0.x, p0), a1 = unpack8_pairs(d0.y, p1);
+      asm volatile("" : "+v"(a0), "+v"(a1));   // step k's unpack comes before step k+1's
+      O[0][k] = mfma16x16x32(a0, bop[0], O[0][k]);
+      O[0][k] = mfma16x16x32(a1, bop[1], O[0][k]);
+      if (k < 7) {
+        asm volatile("" : "+v"(d1), "+v"(q0), "+v"(q1));
+        d0 = d1;
+        p0 = q0;
+        p1 = q1;
+      }
+      if (k < 6) {
+        d1 = dn;
+        q0 = n0;
+        q1 = n1;
+      }
     }
   };
 
@@ -277,9 +303,10 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   };
 
   // ---- query staging.  With two or more tiles per token, the DMA for a later token that
-  // starts at tile i+1 is issued in iteration i just before the row loads of tile i+1, so
-  // at the top of tile i+1 at most those kRowLoads loads may still be in flight.  With one
-  // tile per token the DMA is issued at the top of the tile itself and waited for fully.
+  // starts at tile i+1 is issued in iteration i just before that iteration's index load and
+  // row loads (kRowLoads of them), so at the top of tile i+1 waiting until at most kRowLoads
+  // loads are in flight covers it.  With one tile per token the DMA is issued at the top of
+  // the tile itself and waited for fully.
   const bool lead = cpt > 1;
   Cursor cq;   // tile i+1
   cq.init(c_lo + 1, cpt);
@@ -308,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   cx.init(c_lo, cpt);
   const int32_t v0 = issue_idx(cx);
   cx.next(cpt);
-  int32_t IV = issue_idx(cx);
+  int32_t IV = issue_idx(cx);   // entry of the next tile whose rows are issued
   cx.next(cpt);
   RowRegs RR;
   uint32_t vm = issue_rows(cr, v0, RR);
@@ -329,10 +356,11 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
     const uint32_t vm0 = vm;
     asm volatile("" : "+v"(acc[0]), "+v"(acc[1]) : : "memory");
     stage_q(0);
-    vm = issue_rows(cr, IV, RR);
-    cr.next(cpt);
+    const int32_t vr = IV;
     IV = issue_idx(cx);
     cx.next(cpt);
+    vm = issue_rows(cr, vr, RR);
+    cr.next(cpt);
     __builtin_amdgcn_sched_barrier(0);
     softmax(acc, vm0, 0, m_ref[0]);
     __syncthreads();
@@ -346,6 +374,8 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   // LDS parity: tile i writes codes/sc/pb[i & 1] before its barrier; PV(i-1) reads
   // [(i-1) & 1], written before barrier i-1; tile i+1 writes [(i-1) & 1] again only after
   // barrier i, which every wave passes after its PV(i-1).
+  // The index load of tile i+2 is issued before the row loads of tile i+1, so the wait for
+  // it at the top of iteration i+1 does not wait for them.
   for (int i = 1; i < n; i++) {
     const int par = i & 1, ppar = par ^ 1;
     const bool new_seg = cu.ci == cpt - 1;   // tile i starts a later token
@@ -356,10 +386,10 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
     const uint32_t vmi = vm;
     const uint32_t vb = row_base(cr, IV, vm);   // rows of tile i+1
     cr.next(cpt);
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    qk_refill(RR, par, Q, acc, vb);
     IV = issue_idx(cx);
     cx.next(cpt);
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    qk_refill(RR, par, Q, acc, vb);
     rescale(ppar, fl, bop);
     softmax(acc, vmi, par, new_seg ? -INFINITY : m_ref[0]);
     pv(ppar, bop);
