@@ -16,6 +16,7 @@ namespace {
 using namespace smla;
 
 constexpr int kMinTilesPerWg = 2;     // below this the partial results outweigh the rows
+constexpr int kMinTilesPerSplit = 4;  // few tokens: tiles per split below which the merge outweighs them
 constexpr int kMaxTopk = 65536;
 constexpr uint64_t kMaxBufferBytes = 0xFFFFF000ull;   // byte range of one buffer resource (kOOB)
 
@@ -63,7 +64,7 @@ int32_t auto_splits(bool fp8rows, int32_t T, int32_t H, int32_t topk, bool group
   int64_t G;
   if ((int64_t)T * HB < cus) {
     int64_t S = cus / ((int64_t)T * HB);
-    const int64_t smax = cpt / kMinTilesPerWg;
+    const int64_t smax = cpt / kMinTilesPerSplit;
     if (S > smax) S = smax;
     if (S < 1) S = 1;
     G = (int64_t)T * S;

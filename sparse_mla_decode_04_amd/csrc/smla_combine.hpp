@@ -54,8 +54,8 @@ __device__ __forceinline__ void merge_st1(__amdgpu_buffer_rsrc_t r, uint32_t off
 // and of its lse[NH] within the buffer of `rl`.  out: head 0 of the block (head stride 512
 // fp16); lse_out: head 0.  scratch: >= 2048 floats of LDS.
 //
-// Phase 1: per-head running maximum and denominator of the LSEs, folded by all threads and
-// reduced through LDS.  Phase 2, per chunk of up to 32 splits: the weights
+// More splits than 256 / NH: phase 1, per-head running maximum and denominator of the LSEs,
+// folded by all threads and reduced through LDS.  Phase 2, per chunk of up to 32 splits: the weights
 // exp(lse_s - lse) go to LDS, then the outputs are summed with every load instruction of a
 // wave reading 1 KB of consecutive bytes (thread tid takes 16-byte pieces tid, tid+256, ...
 // of the NH x 512 block, so one thread covers several heads).
@@ -106,7 +106,7 @@ __device__ __forceinline__ void lse_merge_few(int ns, __amdgpu_buffer_rsrc_t ro,
   }
 }
 
-// Up to 2U splits (U = 4 for 16 heads, 2 for 32): the LSEs of every split (one value per
+// 32 heads, up to 2U = 4 splits: the LSEs of every split (one value per
 // thread) and the output pieces of the first U splits in one memory round trip; the
 // per-head maximum, denominator and split weights through LDS; the output pieces of the
 // other splits in a second round trip.
@@ -191,6 +191,98 @@ __device__ __forceinline__ void lse_merge_two(int ns, __amdgpu_buffer_rsrc_t ro,
   }
 }
 
+// 16 heads, up to 16 splits: the LSEs of every split (one value per thread) and the output
+// pieces of the first U splits in one memory round trip; the per-head maximum, denominator
+// and split weights through LDS; the output pieces of the other splits in batches of U, one
+// round trip each.
+template <int NH, int U, bool kCoherent, class PartFn>
+__device__ __forceinline__ void lse_merge_batched(int ns, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
+                                                  PartFn part, f16* out, float* lse_out, float* scratch, int tid,
+                                                  bool active) {
+  constexpr int P = NH / 2;             // 16-byte pieces per thread: piece q is head 2q + tid / 128
+  constexpr int SMAX = 256 / NH;        // splits whose LSEs one value per thread covers
+  float* const ls = scratch;            // [SMAX][NH] LSEs (-inf beyond ns)
+  float* const wt = scratch + 256;      // [SMAX][NH] weights
+  float* const mh = scratch + 512;      // [NH] maximum
+  float* const ih = scratch + 512 + NH; // [NH] 1 / denominator
+  const int h1 = tid >> 7;
+  f32x4 ov[U][P];
+  if (active) {
+    float x = -INFINITY;
+    if (tid < ns * NH) {
+      uint32_t o_off, l_off;
+      part(tid / NH, &o_off, &l_off);
+      x = merge_ld1<kCoherent>(rl, l_off + 4u * (tid % NH));
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {   // ns > U: every one of these splits exists
+      uint32_t o_off, l_off;
+      part(u, &o_off, &l_off);
+#pragma unroll
+      for (int q = 0; q < P; q++) ov[u][q] = merge_ld4<kCoherent>(ro, o_off + 16u * (256 * q + tid));
+    }
+    ls[tid] = x;
+  }
+  __syncthreads();
+  if (active && tid < NH) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < SMAX; s++) m = fmaxf(m, ls[s * NH + tid]);
+    float d = 0.0f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < SMAX; s++) {
+        const float l = ls[s * NH + tid];
+        if (l != -INFINITY) d += __expf(l - m);
+      }
+    }
+    mh[tid] = m;
+    ih[tid] = d > 0.0f ? 1.0f / d : 0.0f;
+    lse_out[tid] = d > 0.0f ? m + logf(d) : -INFINITY;
+  }
+  __syncthreads();
+  if (active) {
+    const int h = tid % NH;
+    const float l = ls[tid];
+    wt[tid] = (l == -INFINITY) ? 0.0f : __expf(l - mh[h]) * ih[h];
+  }
+  __syncthreads();
+  if (!active) return;
+  f32x4 acc[P];
+#pragma unroll
+  for (int q = 0; q < P; q++) {
+    acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U; u++) acc[q] += wt[u * NH + 2 * q + h1] * ov[u][q];
+  }
+  static_assert(NH == 16, "16 heads");
+  constexpr int kMaxBatches = SMAX / U - 1;   // batches after the first
+#pragma unroll
+  for (int bi = 0; bi < kMaxBatches; bi++) {
+    const int b = U * (bi + 1);
+    if (b >= ns) break;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int s = b + u;
+      uint32_t o_off, l_off;
+      part(s < ns ? s : 0, &o_off, &l_off);
+#pragma unroll
+      for (int q = 0; q < P; q++) ov[u][q] = merge_ld4<kCoherent>(ro, o_off + 16u * (256 * q + tid));
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (b + u >= ns) continue;
+#pragma unroll
+      for (int q = 0; q < P; q++) acc[q] += wt[(b + u) * NH + 2 * q + h1] * ov[u][q];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < P; q++) {
+    const int e = 256 * q + tid, h = e / 128, col = 4 * (e % 128);
+    *(f16x4*)(out + 512 * h + col) = f16x4{(f16)acc[q].x, (f16)acc[q].y, (f16)acc[q].z, (f16)acc[q].w};
+  }
+}
+
 template <int NH, bool kCoherent, class PartFn>
 __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rl,
                                           PartFn part, f16* out, float* lse_out, float* scratch, int tid,
@@ -202,9 +294,16 @@ __device__ __forceinline__ void lse_merge(int ns, __amdgpu_buffer_rsrc_t ro, __a
     if (active) lse_merge_few<NH, kFew, kCoherent>(ns, ro, rl, part, out, lse_out, tid);
     return;
   }
-  if (ns <= 2 * U) {
-    lse_merge_two<NH, U, kCoherent>(ns, ro, rl, part, out, lse_out, scratch, tid, active);
-    return;
+  if constexpr (NH == 16) {
+    if (ns <= 256 / NH) {
+      lse_merge_batched<NH, U, kCoherent>(ns, ro, rl, part, out, lse_out, scratch, tid, active);
+      return;
+    }
+  } else {
+    if (ns <= 2 * U) {
+      lse_merge_two<NH, U, kCoherent>(ns, ro, rl, part, out, lse_out, scratch, tid, active);
+      return;
+    }
   }
   constexpr int K = 256 / NH;          // threads per head in phase 1
   constexpr int P = NH / 2;            // 16-byte pieces per thread per split (NH*512*4 / 4096)
