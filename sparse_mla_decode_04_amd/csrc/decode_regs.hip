@@ -389,10 +389,16 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
     IV = issue_idx(cx);
     cx.next(cpt);
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // Wave priority: the two waves sharing a SIMD (from two workgroups) run QK^T at the low
+    // level and softmax and PV, the stretch each workgroup's barrier waits for, at the high
+    // one, so a wave that reaches its tail is issued ahead of the other's matrix work.
+    __builtin_amdgcn_s_setprio(0);
     qk_refill(RR, par, Q, acc, vb);
+    __builtin_amdgcn_s_setprio(1);
     rescale(ppar, fl, bop);
     softmax(acc, vmi, par, new_seg ? -INFINITY : m_ref[0]);
     pv(ppar, bop);
+    __builtin_amdgcn_s_setprio(0);
     segment_end(i - 1);
     __syncthreads();
   }
