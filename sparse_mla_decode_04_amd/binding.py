@@ -388,6 +388,8 @@ def blhnc_copy_blocks(src, dst, src_ids=None, dst_ids=None, n=None):
     seg = seg or dseg
     if n is None:
         n = (src_ids if src_ids is not None else dst_ids if dst_ids is not None else src).shape[0]
+    if n == 0:
+        return dst
     p_src = _dev(src, "src", src.dtype)
     p_dst = _dev(dst, "dst", dst.dtype)
     p_sid = _dev(src_ids, "src_ids", torch.int32) if src_ids is not None else None
