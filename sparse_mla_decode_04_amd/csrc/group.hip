@@ -28,8 +28,8 @@ namespace {
 
 constexpr int kSlotsLog2 = 14;
 constexpr int kSlots = 1 << kSlotsLog2;   // hash table size, twice the largest entry count
-constexpr int kThreadsU = 256;
-constexpr int kPerThread = kMaxGroupEntries / kThreadsU;   // 32 entries per thread, in order
+constexpr int kThreadsU = 1024;
+constexpr int kPerThread = kMaxGroupEntries / kThreadsU;   // 8 entries per thread, in order
 
 struct SmemU {
   int32_t ent[kMaxGroupEntries];  // the group's list entries, read from memory once
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreadsU) void group_union_kernel(const int32_t* _
   }
   __syncthreads();
 
-  // ---- keep the first occurrence of each row; thread tid owns entries 32*tid .. +31
+  // ---- keep the first occurrence of each row; thread tid owns entries kPerThread*tid .. +kPerThread-1
   uint32_t keep = 0;
   int mine = 0;
 #pragma unroll 4
