@@ -272,6 +272,8 @@ SMLA_API int sparse_mla_decode_blhnc(const void* q, const void* pool, int64_t po
                                      int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
   RowMap m;
   if (!blhnc_map(pool_blocks, layers, layer, block_rows, m)) return SMLA_ERR_INVALID_ARG;
+  // layers * block_rows < 2^24 (checked above): bound the blocks first so the product cannot wrap
+  if ((uint64_t)pool_blocks > kMaxBufferBytes / 352) return SMLA_ERR_UNSUPPORTED;
   const uint64_t alloc_rows = (uint64_t)pool_blocks * (uint64_t)layers * (uint64_t)block_rows;
   if (alloc_rows * 352 > kMaxBufferBytes) return SMLA_ERR_UNSUPPORTED;
   return run_decode(Rows::kNvfp4Pool, q, pool, pool_blocks * block_rows, idx, T, H, topk, softmax_scale,

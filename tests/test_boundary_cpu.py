@@ -172,3 +172,9 @@ def test_blhnc_entry_points_check_arguments(L):
     assert cp(P(16), 4, P(2), P(16), 4, None, 2, 16, None) == -1                        # misaligned ids
     assert cp(P(16), 4, None, None, 4, None, 2, 16, None) == -1
     assert cp(P(16), 4, None, P(16), 4, None, 1 << 20, 1 << 20, None) == -2             # grid too large
+
+
+def test_blhnc_decode_rejects_block_counts_that_would_wrap(L):
+    # 2^60 blocks x 16 layers x 16 rows wraps 64 bits; the call must still be refused
+    assert L.sparse_mla_decode_blhnc(P(16), P(16), 1 << 60, 16, 0, 16, P(16), 2, 16, 64, 0.1, P(16), P(16), 0,
+                                     None, 0, None) == -2
