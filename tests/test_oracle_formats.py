@@ -168,6 +168,65 @@ def test_row_layout_matches_hand_worked_example():
     assert bad.size == 0, [(int(i), int(row[i]), int(exp[i])) for i in bad]
 
 
+def _listed(d):
+    return {int(k): float(v) for k, v in d.items()}
+
+
+def test_unpack_decodes_hand_worked_row():
+    # The golden row's expected bytes, decoded back to the values worked out by hand in the
+    # golden file: every latent element not listed is +0.
+    ex = json.load(open(os.path.join(GOLDEN, "row_layout_example.json")))
+    row = np.zeros((1, 352), dtype=np.uint8)
+    for k, v in ex["expected_nonzero_bytes"].items():
+        row[0, int(k)] = v
+    vals = oracle.nvfp4_unpack_rows_ref(row)[0]
+    lat = _listed(ex["decoded_latent_listed"])
+    rope = _listed(ex["decoded_rope"])
+    for e in range(512):
+        assert _same(vals[e], lat.get(e, 0.0)), (e, vals[e], lat.get(e, 0.0))
+    for k in range(64):
+        assert _same(vals[512 + k], rope.get(k, 0.0)), (k, vals[512 + k])
+
+
+def test_unpack_decodes_second_hand_worked_row():
+    # 32 distinct group scales and different codes in the two nibbles of every byte: pins the
+    # nibble order, the element -> group-scale map and the rope offset at the listed elements.
+    ex = json.load(open(os.path.join(GOLDEN, "row_decode_example.json")))
+    row = np.frombuffer(bytes.fromhex(ex["row_hex"]), dtype=np.uint8).reshape(1, 352)
+    vals = oracle.nvfp4_unpack_rows_ref(row)[0]
+    for e, v in _listed(ex["decoded_latent"]).items():
+        assert _same(vals[e], v), (e, vals[e], v)
+    for k, v in _listed(ex["decoded_rope"]).items():
+        assert _same(vals[512 + k], v), (k, vals[512 + k], v)
+
+
+def test_unpack_of_pack_is_a_nearest_grid_point():
+    # Round trip on random rows: each decoded latent value is a point of its group's scaled
+    # E2M1 grid nearest to the input (scale byte decoded by torch's float8_e4m3fn), and each
+    # rope value is torch's E4M3 cast of the input.  A swapped nibble or a wrong group scale
+    # in the decoder moves values off their nearest grid point.
+    rng = np.random.default_rng(23)
+    src = (rng.standard_normal((16, 576)) * rng.choice([0.01, 1, 40], size=(16, 1))).astype(np.float16)
+    rows = oracle.nvfp4_pack_rows_ref(src)
+    vals = oracle.nvfp4_unpack_rows_ref(rows)
+    x = src.astype(np.float64)
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    for i in range(src.shape[0]):
+        scales = torch.from_numpy(rows[i, 256:288].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        for g in range(32):
+            s = scales[g]
+            xs = x[i, 16 * g:16 * g + 16]
+            got = vals[i, 16 * g:16 * g + 16]
+            pts = s * grid
+            for k in range(16):
+                dist = np.abs(np.abs(xs[k]) - pts)
+                assert abs(got[k]) in set(pts[dist == dist.min()]), (i, g, k, xs[k], got[k], s)
+                if got[k] != 0:
+                    assert np.sign(got[k]) == np.sign(xs[k])
+        ref = torch.from_numpy(src[i, 512:].astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        assert np.array_equal(vals[i, 512:], ref)
+
+
 def test_pack_decisions_bruteforce_on_random_rows():
     rng = np.random.default_rng(11)
     src = (rng.standard_normal((24, 576)) * rng.choice([1e-3, 0.1, 1, 30, 3000], size=(24, 1))).astype(np.float16)
