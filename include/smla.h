@@ -86,7 +86,9 @@ SMLA_API int nvfp4_pack_rows(const void* src_dev, const int32_t* slots_dev, int3
                     void* kv_pool_dev, int64_t pool_rows, void* stream);
 
 /*
- * Test / inspection export of the on-chip unpack used by the decode kernels.
+ * Test / inspection export of the on-chip unpack used by the decode kernels ("Four-bit
+ * caches make room": the native kernel unpacks the four-bit rows on chip; this call runs
+ * that same device codec and writes its fp16 result out, so it can be compared bit for bit).
  * Decodes the cache rows rows_dev[i] (i < n) to fp16 out_dev[n][576], bit-exact
  * (latent = E2M1 * E4M3 scale, rope = E4M3).  A row id that is negative or >= pool_rows
  * gives a zero row.
@@ -103,7 +105,8 @@ SMLA_API int nvfp4_unpack_rows_f16(const void* kv_pool_dev, int64_t pool_rows, c
  *   out_dev      fp16 [T][H][512]:  sum_j softmax_j * latent_j over the valid entries
  *   lse_dev      fp32 [T][H]:       ln sum_j exp(softmax_scale * q.k_j)
  * An entry list with no valid entry gives out = 0 and lse = -inf.  Repeated rows count
- * once per entry.  H must be a multiple of 16; 1 <= topk <= 65536.
+ * once per entry.  H must be a multiple of 16; 1 <= topk <= 65536.  softmax_scale must be
+ * finite and > 0 (SMLA_ERR_INVALID_ARG otherwise).
  * Heads are processed in blocks per workgroup: 64 heads when H is a multiple of 64 and
  * topk > 64, else 32 when H is a multiple of 32 and topk > 64, else 16.  A larger block
  * lets one unpack of a row serve more heads.
@@ -125,7 +128,9 @@ SMLA_API int sparse_mla_decode(const void* q_dev, const void* kv_pool_dev, int64
 
 /*
  * The split count the automatic mode of sparse_mla_decode uses for this shape on the
- * current device: with fewer (token, head block) pairs than compute units, every token
+ * current device ("Four-bit caches make room": the kernel sizes its groups of
+ * multiprocessors by the token batch; here the work decomposition is sized by T):
+ * with fewer (token, head block) pairs than compute units, every token
  * is cut into the same number of tile-aligned ranges so that about one workgroup runs
  * per compute unit; otherwise the workgroups that fit the device at once share the tiles
  * (at least two tiles each).  Queries the current device's compute-unit count.
@@ -134,14 +139,18 @@ SMLA_API int sparse_mla_decode(const void* q_dev, const void* kv_pool_dev, int64
 SMLA_API int32_t smla_choose_num_splits(int32_t T, int32_t H, int32_t topk);
 
 /*
- * Workspace bytes sparse_mla_decode needs (num_splits as passed to it, 0 = automatic).
+ * Workspace bytes sparse_mla_decode needs (num_splits as passed to it, 0 = automatic):
+ * the partial results and counters of the batch-sized split work ("Four-bit caches make
+ * room", the sizing by token batch).
  * Also an upper bound for sparse_mla_decode_fp8rows and sparse_mla_decode_fp8pool with
  * the same arguments, whose automatic split count is never larger.
  */
 SMLA_API size_t smla_decode_workspace_bytes(int32_t T, int32_t H, int32_t topk, int32_t num_splits);
 
 /*
- * Log-sum-exp combine of split results (the merge step of the split work above).
+ * Log-sum-exp combine of split results ("Four-bit caches make room": the merge step that
+ * the batch-sized split of each token's index list implies; the decode runs the same merge
+ * inside its own launch, and this call exposes it for partials made elsewhere).
  *   partial_out_dev  fp32 [T][S][H][512]  normalized output of each split
  *   partial_lse_dev  fp32 [T][S][H]       natural-log LSE of each split (-inf = empty split)
  *   out_dev fp16 [T][H][512], lse_dev fp32 [T][H]:

@@ -85,7 +85,8 @@ bool decode_shape_ok(int32_t T, int32_t H, int32_t topk) {
 int check_decode(const void* q, const void* rows, int64_t pool_rows, const int32_t* idx, int32_t T,
                  int32_t H, int32_t topk, float softmax_scale, const void* out, const float* lse,
                  int32_t num_splits) {
-  if (!decode_shape_ok(T, H, topk) || num_splits < 0 || pool_rows < 0 || !isfinite(softmax_scale))
+  if (!decode_shape_ok(T, H, topk) || num_splits < 0 || pool_rows < 0 || !isfinite(softmax_scale) ||
+      !(softmax_scale > 0.f))
     return SMLA_ERR_INVALID_ARG;
   if (H % kHeadGroup != 0) return SMLA_ERR_UNSUPPORTED;
   if (T == 0) return SMLA_OK;

@@ -66,6 +66,9 @@ def test_decode_argument_checks(L):
     assert _decode(L, topk=70000) == -1
     assert _decode(L, ns=-1) == -1
     assert _decode(L, scale=float("nan")) == -1
+    assert _decode(L, scale=float("inf")) == -1
+    assert _decode(L, scale=0.0) == -1             # a zero or negative scale is rejected
+    assert _decode(L, scale=-0.5) == -1
     assert _decode(L, ws=None) == -3               # workspace missing
     assert _decode(L, ws=16, wsb=10) == -3         # workspace too small
     assert _decode(L, T=0, q=None, pool=None, idx=None, out=None, lse=None) == 0   # nothing to do
