@@ -1,12 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse NVFP4 MLA decode hot path on one MI355X.
 
-One step = one pass of the hot path over one batch of the workload: for the
-default workload (35 decode tokens x 16 heads, 2,048-entry index lists over a
-262,144-row NVFP4 pool) that is one sparse_mla_decode launch (gather, on-chip
-unpack, QK^T, online softmax, PV and the in-launch log-sum-exp combine); the
-throughput workload (--config 5) also writes its 1,024 new rows with
-nvfp4_pack_rows first.  Inputs are resident in HBM before timing starts.
+One step = one pass of the hot path over one batch of a workload: one
+sparse_mla_decode launch (gather, on-chip unpack, QK^T, online softmax, PV and the
+in-launch log-sum-exp combine); the 1,024-token throughput workload also writes its
+1,024 new rows with nvfp4_pack_rows first.  Inputs are resident in HBM before timing
+starts.
+
+The default run measures the 1,024-token x 128-head workload with its cache write as
+the headline (the JSON line's top level), then the 1-, 35-, 128- and 264-token
+workloads in the same process (under "configs").  --config k measures only workload k.
 
 Cold caches without a flush in the timed region: every step attends a different
 "layer" -- one of L copies of the pool, L chosen so the copies span >= 2 GiB --
@@ -19,13 +22,15 @@ loop launches decode; --graph 0 launches them one by one from the host), checked
 bit for bit against the eager launch.
 
 Prints one JSON line on stdout.  `value` is decode tokens per second of the
-whole step; `roofline` prices the decode kernel's gathered KV bytes (352 bytes
-per valid list entry) against its average launch duration measured with HIP
-events on the launch stream around a run of back-to-back launches queued behind a
-backlog (so the events bracket the kernels and not the host); `cpu_baseline` times the CPU
-oracle on the host on the same workload.  Untimed for `value`, side legs report
-the staged two-pass variant, session-grouped decode, (`fp8_pool`) the same
-decode over the pool kept as 576-byte FP8 rows, the format NVFP4 replaces, and
+whole step; `roofline` prices the decode kernel's algorithmic work against its
+average launch duration, measured with HIP events on the launch stream around a run
+of back-to-back launches queued behind a backlog (so the events bracket the kernels
+and not the host): gathered KV bytes (352 per valid list entry) against 8 TB/s below
+the ridge (16 heads), matrix flops (2 * H * (576 + 512) per valid entry) against
+2.5 PFLOP/s above it (64 and 128 heads).  `cpu_baseline` times the CPU oracle on the
+host over a token sample of the headline workload.  Untimed for `value`, side legs
+report the staged two-pass variant, session-grouped decode, (`fp8_pool`) the same
+decode over the pool kept as 576-byte FP8 rows, the format NVFP4 replaces,
 (`indexer_topk`) the sparse indexer's top-2,048 selection that produces the lists,
 and (`block_major_pool`) decode and block transfer over the block-major multi-layer
 cache layout.
@@ -99,35 +104,36 @@ def traffic_from_profiles(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, q, idx, src, seconds):
-    """Time the oracle on the host over the workload's tokens (repeating the token list
-    until about `seconds` have passed).  The oracle's rows are quantized beforehand by the
-    oracle's own row writer (untimed), so the timed part is what one GPU launch does:
-    gather, dequant, attention."""
+def cpu_baseline(wl, q, idx, src, seconds, n_tokens):
+    """Time the oracle on the host over a seeded sample of the workload's tokens (repeating
+    the sample until about `seconds` have passed).  The sample's rows are quantized
+    beforehand by the oracle's own row writer (untimed), so the timed part is what one GPU
+    launch does per token: gather, dequant, attention."""
     import oracle
+    from helpers import PackedRows
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas = 1
-    ids = np.unique(idx[idx >= 0])
-    rows = np.zeros((wl.pool_rows, ROW_BYTES), dtype=np.uint8)
-    rows[ids] = oracle.nvfp4_pack_rows_ref(src[ids])
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(6)
+    toks = sorted(rng.choice(wl.T, size=min(wl.T, n_tokens), replace=False).tolist())
+    rows = PackedRows(src, idx[toks].ravel())
     tokens_done = 0
     t0 = time.perf_counter()
-    while True:
-        for t in range(wl.T):
+    while time.perf_counter() - t0 < seconds:
+        for t in toks:
             oracle.sparse_mla_decode_ref(q, rows, idx, wl.softmax_scale, tokens=[t])
             tokens_done += 1
-            if time.perf_counter() - t0 >= seconds and tokens_done >= 1:
+            if time.perf_counter() - t0 >= seconds:
                 break
-        if time.perf_counter() - t0 >= seconds:
-            break
     dt = time.perf_counter() - t0
-    return {"value": tokens_done / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"{tokens_done} decode tokens of the {wl.name} workload (the {wl.T}-token batch "
-                      f"repeated), float64 numpy oracle, {dt:.1f} s; elementwise work single-threaded, "
-                      f"BLAS with {blas} threads"}
+    return {"value": tokens_done / dt, "unit": "tokens/s", "cores": cores, "blas_threads": int(blas),
+            "kind": "oracle",
+            "sample": f"{tokens_done} decode tokens of the {wl.name} workload ({len(toks)} seeded tokens of its "
+                      f"{wl.T}, repeated), float64 numpy oracle, {dt:.1f} s; {cores} cores available, "
+                      f"elementwise work on one thread, BLAS with {blas} threads"}
 
 
 def backlog(torch, ms=20.0):
@@ -467,59 +473,24 @@ def copy_calibration(nbytes=256 << 20, reps=5):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, the 35-token launch)")
-    ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget, 0 disables")
-    ap.add_argument("--check-tokens", type=int, default=3, help="tokens checked against the oracle (untimed)")
-    ap.add_argument("--staged", type=int, default=-1,
-                    help="also time the staged two-pass variant for this many steps "
-                         "(default: 20 for the cache-write workload, else 0)")
-    ap.add_argument("--grouped", type=int, default=-1,
-                    help="also time session-grouped decode (union lists of groups of 64/H tokens, then "
-                         "one pass over them) for this many steps (default: 20 for the agent-mix workload)")
-    ap.add_argument("--fp8pool", type=int, default=50,
-                    help="also time decode over the same pool kept as 576-byte FP8 rows for this many "
-                         "steps (0 disables)")
-    ap.add_argument("--indexer", type=int, default=50,
-                    help="also time the sparse indexer's top-k selection over synthetic scores for this many "
-                         "steps, on workloads whose tokens have a context range (0 disables)")
-    ap.add_argument("--graph", type=int, default=1,
-                    help="1: time the K steps as one replay of a captured HIP graph (default); 0: K eager "
-                         "launches from the host")
-    ap.add_argument("--blhnc", type=int, default=50,
-                    help="launches of the block-major multi-layer pool decode leg, with its block transfer "
-                         "(0 = skip)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
-    args = ap.parse_args()
+LEG_DEFAULTS = {  # side legs and the workloads they run on in the default run
+    "staged": {5}, "grouped": {4}, "fp8pool": {4, 5}, "indexer": {2, 4}, "blhnc": {4},
+}
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(--gpus {args.gpus}, WORLD_SIZE {world}); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
 
+def measure(cfg, args, legs, check_tokens, steps, warmup):
+    """Build workload `cfg`'s inputs on the GPU, time its step (graph replay of `steps`
+    steps) and its decode launch (events around back-to-back launches), check sampled
+    tokens against the oracle, run the side legs in `legs`, and free everything.  Returns
+    (result dict, state for the CPU baseline)."""
     import torch
     import sparse_mla_decode_04_amd as smla
     from sparse_mla_decode_04_amd import binding, workloads as W
     from helpers import OracleRows, build_device_pool, parity_errors, pool_source_all
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    smla.lib()
     dev = "cuda"
-    wl = W.WORKLOADS[args.config]
+    wl = W.WORKLOADS[cfg]
     log(f"workload {wl.name}: T={wl.T} H={wl.H} pool_rows={wl.pool_rows} topk={wl.topk}")
-
     t_setup = time.time()
     src_full = pool_source_all(wl)            # with the workload's new rows at their slots
     new, slots = W.new_rows(wl)
@@ -527,6 +498,7 @@ def main():
     if len(slots):                            # the step writes them; start from the base pool
         src_base = np.concatenate([c for _, c in W.pool_source_chunks(wl)], axis=0)
     pool0 = build_device_pool(src_base, dev)
+    del src_base
     pool_bytes = pool0.numel()
     L = max(2, -(-COLD_SPAN_BYTES // pool_bytes))
     layers = [pool0] + [pool0.clone() for _ in range(L - 1)]
@@ -544,8 +516,8 @@ def main():
         slots_d = torch.from_numpy(slots).to(dev)
         pack = [binding.prepare_pack(new_d, slots_d, p) for p in layers]
     torch.cuda.synchronize()
-    log(f"setup {time.time() - t_setup:.1f}s; {L} layer copies of {pool_bytes / 1e6:.1f} MB; "
-        f"splits {smla.choose_num_splits(wl.T, wl.H, wl.topk) if args.num_splits == 0 else args.num_splits}")
+    splits = args.num_splits or smla.choose_num_splits(wl.T, wl.H, wl.topk)
+    log(f"setup {time.time() - t_setup:.1f}s; {L} layer copies of {pool_bytes / 1e6:.1f} MB; splits {splits}")
 
     n_valid = int(np.sum((idx >= 0) & (idx < wl.pool_rows)))
     kv_bytes = n_valid * ROW_BYTES
@@ -562,32 +534,34 @@ def main():
         if ev is not None:
             ev[1].record()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
     # untimed parity check of the last step's output against the oracle
-    if args.check_tokens > 0:
+    parity = None
+    if check_tokens > 0:
         import oracle
         rng = np.random.default_rng(0)
-        toks = sorted(rng.choice(wl.T, size=min(wl.T, args.check_tokens), replace=False).tolist())
+        toks = sorted(rng.choice(wl.T, size=min(wl.T, check_tokens), replace=False).tolist())
         ref_o, ref_l = oracle.sparse_mla_decode_ref(q, OracleRows(src_full), idx, wl.softmax_scale, tokens=toks)
         oe, le, ok = parity_errors(out.cpu().numpy()[toks], lse.cpu().numpy()[toks], ref_o, ref_l)
         log(f"parity on tokens {toks}: out err {oe:.2e} (tol 2e-3), lse err {le:.2e} (tol 1e-3), -inf ok {ok}")
         if not (oe <= 2e-3 and le <= 1e-3 and ok):
-            print("bench.py: output does not match the oracle", file=sys.stderr)
+            print(f"bench.py: {wl.name} output does not match the oracle", file=sys.stderr)
             sys.exit(3)
+        parity = {"tokens": toks, "out_err": oe, "lse_err": le}
 
     if args.graph:
-        # The K timed steps as one HIP graph (captured, replayed once untimed, then timed):
-        # the host enqueues one replay instead of K launches.  Every step's output is the
-        # same (identical layer copies, the same rows written), so each replay must leave the
+        # The timed steps as one HIP graph (captured, replayed once untimed, then timed): the
+        # host enqueues one replay instead of K launches.  Every step's output is the same
+        # (identical layer copies, the same rows written), so each replay must leave the
         # eager result bit for bit.
         ref_out, ref_lse = out.clone(), lse.clone()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                step(args.warmup + i)
+            for i in range(steps):
+                step(warmup + i)
         graph.replay()
         torch.cuda.synchronize()
         if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
@@ -605,35 +579,32 @@ def main():
         del graph
         # launch durations: a run of eager launches of one kernel queued behind a backlog, one
         # HIP event before and one after the run on the launch stream
-        n_ev = min(args.steps, 200)
+        n_ev = min(max(steps, 50), 200)
 
         def bracket(fn):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             backlog(torch)
             e0.record()
             for i in range(n_ev):
-                fn(args.warmup + args.steps + i)
+                fn(warmup + steps + i)
             e1.record()
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / n_ev
 
-        k_run = bracket(lambda i: decode[i % L]())
-        pack_run = bracket(lambda i: pack[i % L]()) if pack else None
-    else:
-        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(args.warmup + i, evs[i])
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    if args.graph:
-        k_avg = k_run
-        pack_us = pack_run * 1e3 if pack else None
+        k_avg = bracket(lambda i: decode[i % L]())
+        pack_us = bracket(lambda i: pack[i % L]()) * 1e3 if pack else None
+        ms_per_step = (t1 - t0) * 1e3 / steps
         log(f"decode launch: mean {k_avg * 1e3:.2f} us over {n_ev} back-to-back launches; "
             f"step {ms_per_step * 1e3:.2f} us (graph replay)")
     else:
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(warmup + i, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / steps
         kms = np.array([a.elapsed_time(b) for a, b, _ in evs])
         k_avg = float(np.mean(kms))
         pack_us = float(np.mean([c.elapsed_time(a) for a, b, c in evs])) * 1e3 if pack else None
@@ -641,22 +612,8 @@ def main():
             f"min {np.min(kms) * 1e3:.2f} us; step {ms_per_step * 1e3:.2f} us")
     achieved = kv_bytes / (k_avg * 1e-3) / 1e9
     log(f"gathered KV {kv_bytes / 1e6:.2f} MB -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
-
     if pack:
         log(f"cache write ({len(slots)} rows): mean {pack_us:.2f} us")
-    staged_steps = args.staged if args.staged >= 0 else (20 if pack else 0)
-    staged = staged_timing(binding, wl, layers, q_d, idx_d, out, lse, ws, k_avg, staged_steps) if staged_steps else None
-    grouped_steps = args.grouped if args.grouped >= 0 else (20 if wl.name == "agent_mix" else 0)
-    grouped = (grouped_timing(binding, wl, layers, q, q_d, idx, idx_d, src_full, kv_bytes, k_avg, grouped_steps,
-                              args.check_tokens) if grouped_steps else None)
-
-    fp8pool = (fp8pool_timing(binding, wl, q, q_d, idx, idx_d, src_full, n_valid, k_avg, args.fp8pool,
-                              args.check_tokens) if args.fp8pool > 0 else None)
-
-    indexer = indexer_timing(binding, wl, args.indexer, args.check_tokens) if args.indexer > 0 else None
-
-    blhnc = (blhnc_timing(binding, wl, q, q_d, idx, idx_d, src_full, layers, kv_bytes, k_avg, args.blhnc,
-                          args.check_tokens) if args.blhnc > 0 else None)
 
     traffic = traffic_from_profiles(wl.name)
     flops = 2.0 * wl.H * (576 + 512) * n_valid        # QK^T over 576 + PV over 512, per valid entry
@@ -669,41 +626,138 @@ def main():
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
     log(f"matrix work {flops / 1e9:.2f} GFLOP -> {tflops:.1f} TFLOP/s ({tflops / MFMA_F16_PEAK_TFS:.1%} of 2.5 PF)")
     res = {
+        "workload": wl.name, "decode_tokens": wl.T, "heads": wl.H, "topk": wl.topk,
+        "launch": "hip_graph" if args.graph else "eager", "pool_rows": wl.pool_rows, "valid_entries": n_valid,
+        "row_bytes": ROW_BYTES, "cache_write_rows": int(len(slots)), "layer_copies": L, "num_splits": splits,
+        "us_per_launch": k_avg * 1e3, "us_per_step": ms_per_step * 1e3,
+        "tokens_per_s": wl.T / (ms_per_step * 1e-3), "gathered_kv_GBs": achieved,
+        "hbm_frac": achieved / HBM_PEAK_GBS, "tflops": tflops, "mfma_frac": tflops / MFMA_F16_PEAK_TFS,
+        "roofline": roof,
+    }
+    if pack:
+        res["cache_write_us"] = pack_us
+    if parity:
+        res["parity"] = parity
+
+    def leg_steps(name, n):
+        return n if cfg in legs.get(name, ()) else 0
+
+    n = leg_steps("staged", args.staged)
+    if n:
+        res["staged_variant"] = staged_timing(binding, wl, layers, q_d, idx_d, out, lse, ws, k_avg, n)
+    n = leg_steps("grouped", args.grouped)
+    if n:
+        g = grouped_timing(binding, wl, layers, q, q_d, idx, idx_d, src_full, kv_bytes, k_avg, n, check_tokens)
+        if g:
+            res["session_grouped"] = g
+    n = leg_steps("fp8pool", args.fp8pool)
+    if n:
+        res["fp8_pool"] = fp8pool_timing(binding, wl, q, q_d, idx, idx_d, src_full, n_valid, k_avg, n, check_tokens)
+    n = leg_steps("indexer", args.indexer)
+    if n:
+        r = indexer_timing(binding, wl, n, check_tokens)
+        if r:
+            res["indexer_topk"] = r
+    n = leg_steps("blhnc", args.blhnc)
+    if n:
+        r = blhnc_timing(binding, wl, q, q_d, idx, idx_d, src_full, layers, kv_bytes, k_avg, n, check_tokens)
+        if r:
+            res["block_major_pool"] = r
+    del decode, pack, layers, pool0, out, lse, ws, q_d, idx_d
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, (wl, q, idx, src_full)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=0,
+                    help="run only workload 1..5 (as the headline); default 0: the 1,024-token workload as the "
+                         "headline, then workloads 1-4 in the same process (under 'configs')")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget, 0 disables")
+    ap.add_argument("--cpu-tokens", type=int, default=32, help="distinct tokens in the oracle's timed sample")
+    ap.add_argument("--check-tokens", type=int, default=3, help="tokens checked against the oracle (untimed)")
+    ap.add_argument("--staged", type=int, default=20,
+                    help="steps of the staged two-pass variant leg (the 1,024-token workload; 0 disables)")
+    ap.add_argument("--grouped", type=int, default=20,
+                    help="steps of the session-grouped decode leg (union lists of groups of 64/H tokens, then "
+                         "one pass over them; the 264-token workload; 0 disables)")
+    ap.add_argument("--fp8pool", type=int, default=50,
+                    help="launches of decode over the same pool kept as 576-byte FP8 rows (the 264- and "
+                         "1,024-token workloads; 0 disables)")
+    ap.add_argument("--indexer", type=int, default=50,
+                    help="launches of the sparse indexer's top-k selection over synthetic scores (the 35- and "
+                         "264-token workloads; 0 disables)")
+    ap.add_argument("--graph", type=int, default=1,
+                    help="1: time the K steps as one replay of a captured HIP graph (default); 0: K eager "
+                         "launches from the host")
+    ap.add_argument("--blhnc", type=int, default=50,
+                    help="launches of the block-major multi-layer pool decode leg, with its block transfer "
+                         "(the 264-token workload; 0 disables)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (reference for HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus}, WORLD_SIZE {world}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_mla_decode_04_amd as smla
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    smla.lib()
+    head_cfg = args.config or 5
+    # with --config k every leg runs on workload k; the default run places each leg on the
+    # workloads listed in LEG_DEFAULTS
+    legs = {k: {head_cfg} for k in LEG_DEFAULTS} if args.config else LEG_DEFAULTS
+    head, cpu_state = measure(head_cfg, args, legs, args.check_tokens, args.steps, args.warmup)
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(*cpu_state, args.cpu_seconds, args.cpu_tokens)
+        log(f"cpu oracle: {cpu['value']:.1f} tokens/s")
+    del cpu_state
+    others = {}
+    if not args.config:
+        for cfg in (1, 2, 3, 4):
+            r, _ = measure(cfg, args, legs, args.check_tokens, args.steps, min(args.warmup, 10))
+            others[r["workload"]] = r
+    cfg_keys = ("workload", "decode_tokens", "heads", "topk", "launch", "pool_rows", "valid_entries", "row_bytes",
+                "cache_write_rows", "layer_copies", "num_splits", "us_per_launch", "cache_write_us")
+    res = {
         "metric": METRIC,
-        "value": wl.T / (ms_per_step * 1e-3),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["us_per_step"] * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "decode_tokens": wl.T, "heads": wl.H, "topk": wl.topk,
-                   "launch": "hip_graph" if args.graph else "eager",
-                   "pool_rows": wl.pool_rows, "valid_entries": n_valid, "row_bytes": ROW_BYTES,
-                   "cache_write_rows": int(len(slots)), "layer_copies": L,
-                   "num_splits": args.num_splits or smla.choose_num_splits(wl.T, wl.H, wl.topk),
-                   "us_per_launch": k_avg * 1e3},
-        "roofline": roof,
+        "config": {k: head[k] for k in cfg_keys if k in head},
+        "roofline": head["roofline"],
     }
-    if pack:
-        res["config"]["cache_write_us"] = pack_us
-    if staged:
-        res["staged_variant"] = staged
-    if grouped:
-        res["session_grouped"] = grouped
-    if fp8pool:
-        res["fp8_pool"] = fp8pool
-    if indexer:
-        res["indexer_topk"] = indexer
-    if blhnc:
-        res["block_major_pool"] = blhnc
-    if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(wl, q, idx, src_full, args.cpu_seconds)
-        log(f"cpu oracle: {res['cpu_baseline']['value']:.1f} tokens/s")
+    for k in ("parity", "staged_variant", "session_grouped", "fp8_pool", "indexer_topk", "block_major_pool"):
+        if k in head:
+            res[k] = head[k]
+    if others:
+        res["configs"] = others
+    if cpu:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

@@ -98,3 +98,33 @@ def assert_parity(out, lse, ref_out, ref_lse, what=""):
     assert oe <= OUT_RTOL, f"{what}: out error {oe:.3e} > {OUT_RTOL} * max|ref|"
     assert le <= LSE_ATOL, f"{what}: lse error {le:.3e} > {LSE_ATOL}"
     return oe, le
+
+
+class PackedRows:
+    """Pool rows as the oracle sees them for a fixed set of row ids, quantized up front by
+    the oracle's own row writer in worker processes (plain numpy; the workers never touch
+    the GPU).  Indexing with row ids returns uint8 [n, 352] rows; an id outside the set
+    raises."""
+
+    def __init__(self, src, ids, workers=8, chunk=8192):
+        import oracle
+        ids = np.unique(np.asarray(ids, dtype=np.int64))
+        ids = ids[ids >= 0]
+        self.ids = ids
+        parts = [src[ids[a:a + chunk]] for a in range(0, len(ids), chunk)]
+        if len(parts) > 1 and workers > 1:
+            import multiprocessing as mp
+            from concurrent.futures import ProcessPoolExecutor
+            with ProcessPoolExecutor(max_workers=min(workers, len(parts)),
+                                     mp_context=mp.get_context("spawn")) as ex:
+                rows = list(ex.map(oracle.nvfp4_pack_rows_ref, parts))
+        else:
+            rows = [oracle.nvfp4_pack_rows_ref(p) for p in parts]
+        self.rows = np.concatenate(rows, axis=0) if rows else np.zeros((0, 352), dtype=np.uint8)
+
+    def __getitem__(self, ids):
+        ids = np.asarray(ids, dtype=np.int64)
+        pos = np.searchsorted(self.ids, ids)
+        if ids.size and (np.any(pos >= len(self.ids)) or np.any(self.ids[np.minimum(pos, len(self.ids) - 1)] != ids)):
+            raise KeyError("row id not prepared")
+        return self.rows[pos]

@@ -131,3 +131,45 @@ def test_topk_context_longer_than_the_bitmaps(smla):
     got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), 2048, torch.from_numpy(lengths).to(DEV),
                                    torch.from_numpy(off).to(DEV))
     assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, 2048, off))
+
+
+# More tokens than compute units: the 512-thread workgroup form of the selection (smaller
+# per-wave cut-bin buffers, other bin and scan widths) runs instead of the 1,024-thread one.
+MANY_T = 300
+
+
+@pytest.mark.parametrize("kind", ["ties", "grid", "specials", "equal"])
+def test_topk_many_tokens_bit_exact(smla, kind):
+    _say("topk many tokens", kind)
+    rng = np.random.default_rng(["ties", "grid", "specials", "equal"].index(kind) + 700)
+    S = 3000
+    scores = _scores(kind, MANY_T, S, rng)
+    lengths = rng.integers(0, S + 1, size=MANY_T).astype(np.int32)
+    lengths[:4] = [0, 2047, 2048, 2049]
+    off = rng.integers(0, 100000, size=MANY_T).astype(np.int32)
+    for k in (2048, 300):
+        got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), k, torch.from_numpy(lengths).to(DEV),
+                                       torch.from_numpy(off).to(DEV))
+        assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, k, off)), k
+
+
+@pytest.mark.parametrize("kind", ["equal", "three"])
+def test_topk_many_tokens_crowded_cut_bin(smla, kind):
+    rng = np.random.default_rng(41)
+    S = 20000
+    scores = (np.full((MANY_T, S), 0.25, dtype=np.float32) if kind == "equal"
+              else rng.integers(0, 3, size=(MANY_T, S)).astype(np.float32))
+    lengths = rng.integers(2049, S + 1, size=MANY_T).astype(np.int32)
+    for k in (2048, 100):
+        got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), k, torch.from_numpy(lengths).to(DEV))
+        assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, k)), k
+
+
+def test_topk_many_tokens_long_context(smla):
+    rng = np.random.default_rng(42)
+    S = 150000
+    scores = (np.round(rng.standard_normal((MANY_T, S)) * 64) / 64).astype(np.float32)
+    lengths = rng.integers(140000, S + 1, size=MANY_T).astype(np.int32)
+    lengths[:3] = [S, 147457, 147456]
+    got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), 2048, torch.from_numpy(lengths).to(DEV))
+    assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, 2048))
