@@ -127,6 +127,26 @@ SMLA_API int sparse_mla_decode(const void* q_dev, const void* kv_pool_dev, int64
                       void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free variant of sparse_mla_decode, for callers that cannot allocate or pass
+ * device memory for a workspace: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Arguments, result and kernels are those of
+ * sparse_mla_decode without the workspace: the split partials and merge counters live in
+ * a scratch array inside the library, SMLA_NOALLOC_SCRATCH_BYTES on each GPU, held until
+ * the process ends.  The call allocates nothing; it clears the counters it uses with a
+ * small kernel on `stream` before the decode.
+ * A shape whose split work needs more scratch than that (smla_decode_workspace_bytes
+ * above the limit) returns SMLA_ERR_WORKSPACE; pass a smaller num_splits or use
+ * sparse_mla_decode with a workspace.  All calls on one GPU share its scratch: calls that
+ * overlap on one GPU (concurrent streams, or threads) race and give wrong results; calls
+ * on one stream, one after another, are safe.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+SMLA_API int sparse_mla_decode_noalloc(const void* q_dev, const void* kv_pool_dev, int64_t pool_rows,
+                                       const int32_t* indices_dev, int32_t T, int32_t H, int32_t topk,
+                                       float softmax_scale, void* out_dev, float* lse_dev, int32_t num_splits,
+                                       void* stream);
+
+/*
  * The split count the automatic mode of sparse_mla_decode uses for this shape on the
  * current device ("Four-bit caches make room": the kernel sizes its groups of
  * multiprocessors by the token batch; here the work decomposition is sized by T):

@@ -10,5 +10,5 @@ from .binding import (  # noqa: F401
     sparse_mla_combine, nvfp4_stage_fp8, sparse_mla_decode_fp8rows, choose_num_splits,
     decode_workspace_bytes, make_workspace, group_union, sparse_mla_decode_grouped, grouped_workspace_bytes,
     make_grouped_workspace, fp8_pack_rows, sparse_mla_decode_fp8pool, sparse_indexer_topk,
-    nvfp4_pack_rows_blhnc, sparse_mla_decode_blhnc, blhnc_copy_blocks,
+    nvfp4_pack_rows_blhnc, sparse_mla_decode_blhnc, blhnc_copy_blocks, sparse_mla_decode_noalloc,
 )

@@ -32,6 +32,7 @@ _SIGS = {
     "nvfp4_pack_rows": ([_P, _P, _I32, _P, _I64, _P], ctypes.c_int),
     "nvfp4_unpack_rows_f16": ([_P, _I64, _P, _I32, _P, _P], ctypes.c_int),
     "sparse_mla_decode": ([_P, _P, _I64, _P, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P], ctypes.c_int),
+    "sparse_mla_decode_noalloc": ([_P, _P, _I64, _P, _I32, _I32, _I32, _F32, _P, _P, _I32, _P], ctypes.c_int),
     "smla_choose_num_splits": ([_I32, _I32, _I32], _I32),
     "smla_decode_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
     "sparse_mla_combine": ([_P, _P, _I32, _I32, _I32, _P, _P, _P], ctypes.c_int),
@@ -173,6 +174,27 @@ def sparse_mla_decode(q, kv_pool, indices, softmax_scale, out=None, lse=None, nu
         raise ValueError("kv_pool must be uint8 [N, 352]")
     return _decode_common("sparse_mla_decode", q, _dev(kv_pool, "kv_pool", torch.uint8), kv_pool.shape[0],
                           indices, softmax_scale, out, lse, num_splits, workspace)
+
+
+def sparse_mla_decode_noalloc(q, kv_pool, indices, softmax_scale, out=None, lse=None, num_splits=0):
+    """sparse_mla_decode without a workspace: the library's own scratch holds the split
+    partials (SMLA_NOALLOC_SCRATCH_BYTES per GPU; calls overlapping on one GPU race)."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be fp16 [T, H, 576]")
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != ROW_BYTES:
+        raise ValueError("kv_pool must be uint8 [N, 352]")
+    T, H, _ = q.shape
+    topk = indices.shape[1]
+    if out is None:
+        out = torch.empty((T, H, LATENT_DIM), dtype=torch.float16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _check(lib().sparse_mla_decode_noalloc(
+        _dev(q, "q", torch.float16, (T, H, HEAD_DIM)), _dev(kv_pool, "kv_pool", torch.uint8),
+        ctypes.c_int64(kv_pool.shape[0]), _dev(indices, "indices", torch.int32, (T, topk)), T, H, topk,
+        ctypes.c_float(softmax_scale), _dev(out, "out", torch.float16, (T, H, LATENT_DIM)),
+        _dev(lse, "lse", torch.float32, (T, H)), int(num_splits), _stream()), "sparse_mla_decode_noalloc")
+    return out, lse
 
 
 def sparse_mla_combine(partial_out, partial_lse, out=None, lse=None):

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "smla.h"
 #include "smla_decode.hpp"
@@ -96,6 +97,35 @@ int check_decode(const void* q, const void* rows, int64_t pool_rows, const int32
   return SMLA_OK;
 }
 
+// Scratch of sparse_mla_decode_noalloc (partials, their LSEs and the merge counters of
+// the split work), one copy per GPU, held until the process ends.  Host code never uses
+// this name as an address: scratch_address() looks up each device's copy.
+static __device__ __align__(256) unsigned char scratch[SMLA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device: hipGetSymbolAddress once per device,
+// with that device current (each GPU holds its own copy at its own address); nullptr if the
+// lookup fails.
+void* scratch_address() {
+  static std::atomic<void*> addr[64];
+  static std::mutex mu;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+__global__ void zero_words_kernel(int32_t* p, int32_t n) {
+  const int32_t i = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0;
+}
+
 // What `rows` holds: the NVFP4 pool, the staged FP8 rows of pass 2 (one per list entry),
 // or a pool of FP8 rows.
 enum class Rows { kNvfp4Pool, kFp8Staged, kFp8Pool };
@@ -105,7 +135,8 @@ enum class Rows { kNvfp4Pool, kFp8Staged, kFp8Pool };
 int run_decode(Rows kind, const void* q, const void* rows, int64_t pool_rows,
                const int32_t* idx, int32_t T, int32_t H, int32_t topk, float softmax_scale,
                void* out, float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream,
-               int32_t tok_heads = 0, const RowMap& map = identity_rowmap(), uint64_t alloc_rows = 0) {
+               int32_t tok_heads = 0, const RowMap& map = identity_rowmap(), uint64_t alloc_rows = 0,
+               bool clear_counters = false) {
   const bool grouped = tok_heads > 0;
   const bool fp8rows = kind != Rows::kNvfp4Pool;
   int st = check_decode(q, rows, pool_rows, idx, T, H, topk, softmax_scale, out, lse, num_splits);
@@ -150,6 +181,12 @@ int run_decode(Rows kind, const void* q, const void* rows, int64_t pool_rows,
   a.tok_heads = tok_heads;
   a.fp8_pool = kind == Rows::kFp8Pool;
   a.map = map;
+  if (clear_counters) {   // a zero-fill kernel, not a memset node, so the call can be captured
+    const int32_t n = p.HB * T;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                       a.counters, n);
+    if (hipGetLastError() != hipSuccess) return SMLA_ERR_LAUNCH;
+  }
   const hipError_t e = grouped ? launch_decode_grouped(a, (hipStream_t)stream)
                        : fp8rows ? launch_decode_fp8rows(a, (hipStream_t)stream)
                                  : launch_decode_nvfp4(a, (hipStream_t)stream, decode_variant());
@@ -265,6 +302,18 @@ SMLA_API int sparse_mla_decode(const void* q, const void* pool, int64_t pool_row
                       float* lse, int32_t num_splits, void* ws, size_t ws_bytes, void* stream) {
   return run_decode(Rows::kNvfp4Pool, q, pool, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
                     num_splits, ws, ws_bytes, stream);
+}
+
+SMLA_API int sparse_mla_decode_noalloc(const void* q, const void* pool, int64_t pool_rows, const int32_t* idx,
+                                       int32_t T, int32_t H, int32_t topk, float softmax_scale, void* out,
+                                       float* lse, int32_t num_splits, void* stream) {
+  // argument errors first, as in sparse_mla_decode, before the device lookup
+  const int st = check_decode(q, pool, pool_rows, idx, T, H, topk, softmax_scale, out, lse, num_splits);
+  if (st != SMLA_OK || T == 0) return st;
+  void* ws = scratch_address();
+  if (ws == nullptr) return SMLA_ERR_LAUNCH;
+  return run_decode(Rows::kNvfp4Pool, q, pool, pool_rows, idx, T, H, topk, softmax_scale, out, lse,
+                    num_splits, ws, SMLA_NOALLOC_SCRATCH_BYTES, stream, 0, identity_rowmap(), 0, true);
 }
 
 SMLA_API int sparse_mla_decode_blhnc(const void* q, const void* pool, int64_t pool_blocks, int32_t layers,

@@ -74,6 +74,17 @@ def test_decode_argument_checks(L):
     assert _decode(L, T=0, q=None, pool=None, idx=None, out=None, lse=None) == 0   # nothing to do
 
 
+def test_noalloc_decode_argument_checks(L):
+    # argument errors come back before the library looks up its scratch on a device
+    f = L.sparse_mla_decode_noalloc
+    assert f(None, P(16), 100, P(16), 1, 16, 64, 0.1, P(16), P(16), 0, None) == -1
+    assert f(P(16), P(16), 100, P(16), 1, 24, 64, 0.1, P(16), P(16), 0, None) == -2
+    assert f(P(16), P(16), 100, P(16), 1, 16, 64, 0.0, P(16), P(16), 0, None) == -1
+    assert f(P(16), P(16), 100, P(16), 1, 16, 0, 0.1, P(16), P(16), 0, None) == -1
+    assert f(P(16), P(16), 100, P(16), 1, 16, 64, 0.1, P(16), P(16), -2, None) == -1
+    assert f(None, None, 100, None, 0, 16, 64, 0.1, None, None, 0, None) == 0    # T == 0: nothing to do
+
+
 def test_other_entry_points_check_arguments(L):
     assert L.nvfp4_pack_rows(None, None, 0, None, 10, None) == 0        # n == 0: no-op
     assert L.nvfp4_pack_rows(None, P(16), 3, P(16), 10, None) == -1
