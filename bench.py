@@ -321,10 +321,12 @@ def indexer_timing(binding, wl, steps, check_tokens):
     len_d = torch.from_numpy(lengths).to("cuda")
     off_d = torch.from_numpy(off).to("cuda")
     out = torch.empty((wl.T, wl.topk), dtype=torch.int32, device="cuda")
+    ws = binding.make_indexer_workspace(wl.T, scores.shape[1], wl.topk)   # None: one workgroup per token
     for i in range(3):
-        binding.sparse_indexer_topk(copies[i % L], wl.topk, len_d, off_d, out)
+        binding.sparse_indexer_topk(copies[i % L], wl.topk, len_d, off_d, out, workspace=ws)
     torch.cuda.synchronize()
-    res = {"scores_per_token": int(scores.shape[1]), "score_copies": L}
+    res = {"scores_per_token": int(scores.shape[1]), "score_copies": L,
+           "workgroups_per_token": "split" if ws is not None else 1}
     if check_tokens > 0:
         rng = np.random.default_rng(3)
         toks = sorted(rng.choice(wl.T, size=min(wl.T, check_tokens), replace=False).tolist())
@@ -337,7 +339,7 @@ def indexer_timing(binding, wl, steps, check_tokens):
     backlog(torch)
     for i in range(steps):
         evs[i][0].record()
-        binding.sparse_indexer_topk(copies[(3 + i) % L], wl.topk, len_d, off_d, out)
+        binding.sparse_indexer_topk(copies[(3 + i) % L], wl.topk, len_d, off_d, out, workspace=ws)
         evs[i][1].record()
     torch.cuda.synchronize()
     us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3

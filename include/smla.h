@@ -241,12 +241,28 @@ SMLA_API int sparse_mla_decode_fp8pool(const void* q_dev, const void* fp8_pool_d
  *                   (-0 equals +0) going to the lower position, as row_offset[t] + position
  *                   in ascending position order; a token with fewer than k positions lists
  *                   them all, then -1.  Entries must fit int32.
+ *   parts           workgroups per token: 0 = chosen by the library, 1 = one (no workspace),
+ *                   2 .. 64 = the token's positions split over that many (needs a workspace;
+ *                   T <= 65535).  The result does not depend on it.
+ *   workspace_dev   device scratch of smla_indexer_workspace_bytes(T, ld, k, parts) bytes,
+ *                   16-byte aligned, zero-filled before its first use and left so by every
+ *                   call; NULL runs one workgroup per token (parts 0 or 1).  Calls that share
+ *                   a workspace must not overlap.
  * 1 <= k <= 65536; ld >= 0 a multiple of 4, below 2^31; scores_dev 16-byte aligned (may be
- * NULL when ld == 0).  One workgroup per token.
+ * NULL when ld == 0).  SMLA_ERR_WORKSPACE when a split is asked for without a large enough
+ * workspace.
  */
 SMLA_API int sparse_indexer_topk(const float* scores_dev, int64_t ld, const int32_t* lengths_dev,
                                  const int32_t* row_offset_dev, int32_t T, int32_t k, int32_t* out_dev,
-                                 void* stream);
+                                 int32_t parts, void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes of sparse_indexer_topk for these arguments (0: it runs one workgroup per
+ * token and needs none, or the arguments are invalid).  With few tokens the library splits
+ * every token's positions over several workgroups so that the selection fills the GPU
+ * ("Four-bit caches make room": the decomposition is sized by the token batch).
+ */
+SMLA_API size_t smla_indexer_workspace_bytes(int32_t T, int64_t ld, int32_t k, int32_t parts);
 
 /*
  * Grouped decode, step 1: union lists of token groups.  "Prime Intellect Launches Prime

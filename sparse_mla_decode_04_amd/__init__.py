@@ -11,4 +11,5 @@ from .binding import (  # noqa: F401
     decode_workspace_bytes, make_workspace, group_union, sparse_mla_decode_grouped, grouped_workspace_bytes,
     make_grouped_workspace, fp8_pack_rows, sparse_mla_decode_fp8pool, sparse_indexer_topk,
     nvfp4_pack_rows_blhnc, sparse_mla_decode_blhnc, blhnc_copy_blocks, sparse_mla_decode_noalloc,
+    indexer_workspace_bytes, make_indexer_workspace,
 )

@@ -41,7 +41,8 @@ _SIGS = {
     "fp8_pack_rows": ([_P, _P, _I32, _P, _I64, _P], ctypes.c_int),
     "sparse_mla_decode_fp8pool": ([_P, _P, _I64, _P, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P],
                                   ctypes.c_int),
-    "sparse_indexer_topk": ([_P, _I64, _P, _P, _I32, _I32, _P, _P], ctypes.c_int),
+    "sparse_indexer_topk": ([_P, _I64, _P, _P, _I32, _I32, _P, _I32, _P, _SZ, _P], ctypes.c_int),
+    "smla_indexer_workspace_bytes": ([_I32, _I64, _I32, _I32], _SZ),
     "smla_group_union": ([_P, _I32, _I32, _I32, _I64, _I32, _P, _P, _P], ctypes.c_int),
     "sparse_mla_decode_grouped": ([_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _F32, _P, _P, _I32, _P, _SZ, _P],
                                   ctypes.c_int),
@@ -301,9 +302,22 @@ def prepare_pack(src, slots, kv_pool):
 
 # ---------------------------------------------------------------- sparse indexer ---
 
-def sparse_indexer_topk(scores, k, lengths=None, row_offset=None, out=None):
+def indexer_workspace_bytes(T, S, k, parts=0):
+    return int(lib().smla_indexer_workspace_bytes(T, S, k, parts))
+
+
+def make_indexer_workspace(T, S, k, parts=0, device="cuda"):
+    """Zero-filled workspace for sparse_indexer_topk (uint8 tensor), or None when the call
+    runs one workgroup per token."""
+    nb = indexer_workspace_bytes(T, S, k, parts)
+    return torch.zeros(nb, dtype=torch.uint8, device=device) if nb > 0 else None
+
+
+def sparse_indexer_topk(scores, k, lengths=None, row_offset=None, out=None, parts=0, workspace=None):
     """Top-k selection over scores float32 [T, S] (S a multiple of 4): int32 [T, k] lists of
-    row_offset[t] + position, ascending, -1 past a token's length."""
+    row_offset[t] + position, ascending, -1 past a token's length.  parts: workgroups per
+    token (0 = the library's choice); a workspace is made when the call needs one and none is
+    given."""
     if scores.dim() != 2:
         raise ValueError("scores must be float32 [T, S]")
     T, S = scores.shape
@@ -311,8 +325,13 @@ def sparse_indexer_topk(scores, k, lengths=None, row_offset=None, out=None):
         out = torch.empty((T, k), dtype=torch.int32, device=scores.device)
     p_len = _dev(lengths, "lengths", torch.int32, (T,)) if lengths is not None else None
     p_off = _dev(row_offset, "row_offset", torch.int32, (T,)) if row_offset is not None else None
+    if workspace is None:
+        workspace = make_indexer_workspace(T, S, k, parts, scores.device)
+    p_ws = _dev(workspace, "workspace", torch.uint8) if workspace is not None else None
+    nb = workspace.numel() if workspace is not None else 0
     _check(lib().sparse_indexer_topk(_dev(scores, "scores", torch.float32), S, p_len, p_off, T, k,
-                                     _dev(out, "out", torch.int32, (T, k)), _stream()), "sparse_indexer_topk")
+                                     _dev(out, "out", torch.int32, (T, k)), int(parts), p_ws, nb, _stream()),
+           "sparse_indexer_topk")
     return out
 
 

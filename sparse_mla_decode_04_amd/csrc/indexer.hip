@@ -11,7 +11,9 @@
 //   * entries are row_offset[t] + position, in ascending position order; a token with fewer
 //     than k positions lists them all, then -1.
 //
-// One workgroup per token: 1,024 threads when the tokens fit the CUs once, else 512.
+// One workgroup per token: 1,024 threads when the tokens fit the CUs once, else 512.  With
+// at most half as many tokens as CUs, each token's positions are split over several
+// workgroups instead (indexer_split.hpp), given a workspace.
 // Scores map to 32-bit keys whose unsigned order is the numbers' order; the k-th largest
 // key K is found by a radix select over 11, 11 and 10 key bits (each step histograms, in
 // LDS, the keys that share the bits chosen so far; a prefix sum over the bins from the top
@@ -40,6 +42,7 @@ namespace {
 namespace wg1024 {
 constexpr int kThreadsK = 1024;
 #include "indexer_body.hpp"
+#include "indexer_split.hpp"
 }  // namespace wg1024
 namespace wg512 {
 constexpr int kThreadsK = 512;
@@ -62,16 +65,57 @@ int device_cus() {
 
 bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+constexpr int kMaxParts = 64;        // workgroups per token of the split selection
+constexpr int64_t kMinChunk = 8192;  // positions per workgroup the automatic split keeps at least
+
+// Workgroups per token: `parts` when given, else a split that fills the CUs once when the
+// tokens fill at most half of them (each chunk keeping kMinChunk positions), else 1.
+int32_t indexer_parts(int32_t T, int64_t ld, int32_t parts) {
+  if (parts > 0) return parts;
+  const int cus = device_cus();
+  if (T < 1 || 2 * (int64_t)T > cus) return 1;
+  int64_t P = cus / T;
+  if (P > kMaxParts) P = kMaxParts;
+  if (P > ld / kMinChunk) P = ld / kMinChunk;
+  return P >= 2 ? (int32_t)P : 1;
+}
+
+bool indexer_args_ok(int32_t T, int64_t ld, int32_t k, int32_t parts) {
+  return T >= 0 && k >= 1 && k <= wg512::kMaxK && ld >= 0 && ld % 4 == 0 && ld <= INT32_MAX && parts >= 0 &&
+         parts <= kMaxParts;
+}
+
 }  // namespace
+
+extern "C" SMLA_API size_t smla_indexer_workspace_bytes(int32_t T, int64_t ld, int32_t k, int32_t parts) {
+  if (!indexer_args_ok(T, ld, k, parts) || T == 0) return 0;
+  const int32_t P = indexer_parts(T, ld, parts);
+  if (P < 2 || T > 65535) return 0;
+  return wg1024::split_ws_layout(T, P, nullptr, nullptr);
+}
 
 extern "C" SMLA_API int sparse_indexer_topk(const float* scores, int64_t ld, const int32_t* lengths,
                                             const int32_t* row_offset, int32_t T, int32_t k, int32_t* out,
-                                            void* stream) {
-  if (T < 0 || k < 1 || k > wg512::kMaxK || ld < 0 || ld % 4 != 0 || ld > INT32_MAX) return SMLA_ERR_INVALID_ARG;
+                                            int32_t parts, void* ws, size_t ws_bytes, void* stream) {
+  if (!indexer_args_ok(T, ld, k, parts)) return SMLA_ERR_INVALID_ARG;
   if (T == 0) return SMLA_OK;
   if (!out || !aligned_to(out, 4) || (ld > 0 && (!scores || !aligned_to(scores, 16))) ||
       (lengths && !aligned_to(lengths, 4)) || (row_offset && !aligned_to(row_offset, 4)))
     return SMLA_ERR_INVALID_ARG;
+  const int32_t P = indexer_parts(T, ld, parts);
+  if (P >= 2 && T > 65535) return SMLA_ERR_UNSUPPORTED;   // the split launches put tokens on grid y
+  if (P >= 2 && ws != nullptr) {
+    if (!aligned_to(ws, 16) || ws_bytes < wg1024::split_ws_layout(T, P, nullptr, nullptr)) return SMLA_ERR_WORKSPACE;
+    wg1024::SplitWs v;
+    wg1024::split_ws_layout(T, P, ws, &v);
+    const hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(wg1024::topk_split_hist_kernel, dim3(P, T), dim3(wg1024::kThreadsK), 0, s, scores, ld,
+                       lengths, k, P, v);
+    hipLaunchKernelGGL(wg1024::topk_split_classify_kernel, dim3(P, T), dim3(wg1024::kThreadsK), 0, s, scores, ld,
+                       lengths, row_offset, k, P, out, v);
+    return hipGetLastError() == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+  }
+  if (parts >= 2) return SMLA_ERR_WORKSPACE;   // a split asked for without a workspace
   if (T <= device_cus())
     hipLaunchKernelGGL(wg1024::sparse_indexer_topk_kernel, dim3(T), dim3(wg1024::kThreadsK), 0, (hipStream_t)stream,
                        scores, ld, lengths, row_offset, k, out);

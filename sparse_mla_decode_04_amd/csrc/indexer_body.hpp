@@ -156,12 +156,11 @@ __device__ __forceinline__ void for_keys_global(const float* __restrict__ s, int
   });
 }
 
-// One radix step: histogram of bits (shift .. shift + log2(bmask + 1)) of the keys that
-// match `prefix` under `pmask`, then the bin of the need-th largest; narrows prefix / pmask
-// and takes the keys of higher bins off `need`.  `visit(f)` calls f(key) for every key.
+// Histogram, in sm.hist, of bits shift .. shift + log2(bmask + 1) of the keys that match
+// `prefix` under `pmask`; `visit(f)` calls f(key, position) for every key.
 template <class V>
-__device__ __forceinline__ void radix_step(SmemTopk& sm, V visit, int shift, uint32_t bmask, uint32_t& prefix,
-                                           uint32_t& pmask, uint32_t& need) {
+__device__ __forceinline__ void radix_hist(SmemTopk& sm, V visit, int shift, uint32_t bmask, uint32_t prefix,
+                                           uint32_t pmask) {
   const int tid = threadIdx.x;
   for (int i = tid; i < kBins; i += kThreadsK) sm.hist[i] = 0;
   __syncthreads();
@@ -170,6 +169,13 @@ __device__ __forceinline__ void radix_step(SmemTopk& sm, V visit, int shift, uin
     if ((key & pm) == pf) atomicAdd(&sm.hist[(key >> shift) & bmask], 1u);
   });
   __syncthreads();
+}
+
+// The bin of sm.hist (bins 0 .. bmask) holding the need-th largest key; narrows prefix /
+// pmask and takes the keys of higher bins off `need`.
+__device__ __forceinline__ void radix_pick(SmemTopk& sm, int shift, uint32_t bmask, uint32_t& prefix,
+                                           uint32_t& pmask, uint32_t& need) {
+  const int tid = threadIdx.x;
   // thread tid holds the kPerBins bins of descending rank kPerBins tid .. + kPerBins - 1
   constexpr int kPerBins = kBins / kThreadsK;
   uint32_t h[kPerBins], sum = 0;
@@ -194,6 +200,14 @@ __device__ __forceinline__ void radix_step(SmemTopk& sm, V visit, int shift, uin
   pmask |= bmask << shift;
   need -= sm.pick[1];
   __syncthreads();
+}
+
+// One radix step: the histogram, then the bin of the need-th largest key.
+template <class V>
+__device__ __forceinline__ void radix_step(SmemTopk& sm, V visit, int shift, uint32_t bmask, uint32_t& prefix,
+                                           uint32_t& pmask, uint32_t& need) {
+  radix_hist(sm, visit, shift, bmask, prefix, pmask);
+  radix_pick(sm, shift, bmask, prefix, pmask, need);
 }
 
 // The list from `cnt` (key, position) pairs in position order, given by at(i, key, pos):
@@ -238,6 +252,154 @@ __device__ __forceinline__ void emit(SmemTopk& sm, int64_t cnt, A at, uint32_t K
   }
 }
 
+// Pass 2 over the n scores at s (positions relative to s): keys in bins above `cut` set
+// their bits in sm.above (word p >> 5); keys in bin `cut` go with their positions to their
+// wave's region of sm.ckey / sm.cpos.  Afterwards sm.wcut[w] holds the keys of the cut bin
+// wave w found (more than kCapWave: its region overflowed).  sm.above must be zero.
+__device__ __forceinline__ void classify_pass(SmemTopk& sm, const float* __restrict__ s, int64_t n, uint32_t cut) {
+  const int tid = threadIdx.x;
+  // opaque to the optimizer, which would otherwise turn the sign-bit tests below back into
+  // compare-and-select pairs
+  asm volatile("" : "+v"(cut));
+  const int wave = tid >> 6;
+  uint32_t wfill = 0;   // keys of the cut bin this wave found so far (uniform in the wave)
+  // one round.  The 4 positions of a 16-byte load share one bitmap word (they start at a
+  // multiple of 4), so each load sets its bits with one OR (of 0 when none is above the
+  // cut).  A lane's cut-bin keys go to its wave's region after those of lower lanes: the
+  // wave prefix sum of the counts (below 32) is built from ballots of their five bits.
+  auto round = [&](const uint32_t (&key)[4 * kVec], int64_t c, bool full) {
+    uint32_t cutm[kVec], m = 0;
+#pragma unroll
+    for (int j = 0; j < kVec; j++) {
+      const int64_t p = c + 4 * (tid + (int64_t)kThreadsK * j);
+      uint32_t am = 0, cm = 0;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        // bins are below 2^11: cut - b is negative exactly when b > cut, and
+        // (b ^ cut) - 1 exactly when b == cut
+        const uint32_t b = key[4 * j + e] >> 21;
+        uint32_t above = (cut - b) >> 31, equal = ((b ^ cut) - 1u) >> 31;
+        if (!full && p + e >= n) above = equal = 0;
+        am |= above << e;
+        cm |= equal << e;
+      }
+      if (p < n) atomicOr(&sm.above[p >> 5], am << (p & 31));
+      cutm[j] = cm;
+      m += __builtin_popcount(cm);
+    }
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int bit = 0; bit < 5; bit++) {
+      const uint64_t bal = __ballot((m >> bit) & 1u);
+      before += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))
+                << bit;
+      total += (uint32_t)__popcll(bal) << bit;
+    }
+    if (m != 0) {
+      uint32_t i = wfill + before;
+#pragma unroll
+      for (int j = 0; j < kVec; j++) {
+        if (cutm[j] == 0) continue;
+        const int64_t p = c + 4 * (tid + (int64_t)kThreadsK * j);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          if ((cutm[j] >> e) & 1u) {
+            if (i < (uint32_t)kCapWave) {
+              sm.ckey[wave * kCapWave + i] = key[4 * j + e];
+              sm.cpos[wave * kCapWave + i] = (int32_t)(p + e);
+            }
+            i++;
+          }
+        }
+      }
+    }
+    wfill += total;
+  };
+  for_rounds(s, n, round);
+  if ((tid & 63) == 0) sm.wcut[wave] = wfill;
+  __syncthreads();
+}
+
+// The rest of the selection in LDS, once pass 1 has picked the top-11-bit bin (prefix /
+// pmask / need): the keys above that bin are bits of sm.above[0, W), the cut bin's keys and
+// positions are in sm.ckey / sm.cpos (entry i holds one when kept(i)), sm.tie is zero.  The
+// two remaining radix steps give K and how many keys equal to K the list takes; the list is
+// written in position order from the bitmaps.
+template <class Kept>
+__device__ __forceinline__ void finish_in_lds(SmemTopk& sm, Kept kept, uint32_t prefix, uint32_t pmask, uint32_t need,
+                                              int64_t W, int32_t off, int32_t* __restrict__ o, int32_t k) {
+  const int tid = threadIdx.x;
+  auto lds_keys = [&](auto f) {
+    for (int i = tid; i < kCap; i += kThreadsK)
+      if (kept(i)) f(sm.ckey[i], (int64_t)0);
+  };
+  radix_step(sm, lds_keys, 10, 2047u, prefix, pmask, need);
+  radix_step(sm, lds_keys, 0, 1023u, prefix, pmask, need);
+  const uint32_t K = prefix;
+  for (int i = tid; i < kCap; i += kThreadsK) {
+    if (!kept(i)) continue;
+    const uint32_t key = sm.ckey[i];
+    const int32_t p = sm.cpos[i];
+    if (key > K) atomicOr(&sm.above[p >> 5], 1u << (p & 31));
+    else if (key == K) atomicOr(&sm.tie[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  // ---- the list from the bitmaps: thread tid takes words [w0, w1); a set bit of `above`
+  // goes to gb + min(eb, need), one of `tie` to gb + eb while eb < need (gb / eb: bits of
+  // `above` / `tie` at lower positions)
+  const int per = (int)((W + kThreadsK - 1) / kThreadsK);
+  const int w0 = tid * per, w1 = (int)(w0 + per < W ? w0 + per : W);
+  uint32_t g = 0, e = 0;
+  for (int w = w0; w < w1; w++) {
+    g += __builtin_popcount(sm.above[w]);
+    e += __builtin_popcount(sm.tie[w]);
+  }
+  uint32_t tot;
+  uint32_t gb = block_scan(sm, g, tot) - g;
+  uint32_t eb = block_scan(sm, e, tot) - e;
+  for (int w = w0; w < w1; w++) {
+    const uint32_t a = sm.above[w], t = sm.tie[w];
+    uint32_t m = a | t;
+    while (m) {
+      const int bit = __builtin_ctz(m);
+      m &= m - 1;
+      const int32_t entry = off + (w * 32 + bit);
+      // the places are below k by construction; the test only keeps a write inside the row
+      if ((a >> bit) & 1u) {
+        const uint32_t place = gb + (eb < need ? eb : need);
+        if (place < (uint32_t)k) o[place] = entry;
+        gb++;
+      } else {
+        if (eb < need && gb + eb < (uint32_t)k) o[gb + eb] = entry;
+        eb++;
+      }
+    }
+  }
+}
+
+// The same from the n scores at s in memory: a context longer than the bitmaps, or a cut bin
+// with more keys than LDS keeps.
+__device__ __forceinline__ void finish_in_memory(SmemTopk& sm, const float* __restrict__ s, int64_t n,
+                                                 uint32_t prefix, uint32_t pmask, uint32_t need, int32_t off,
+                                                 int32_t* __restrict__ o, int32_t k) {
+  auto global_keys = [&](auto f) { for_keys_global(s, n, f); };
+  radix_step(sm, global_keys, 10, 2047u, prefix, pmask, need);
+  radix_step(sm, global_keys, 0, 1023u, prefix, pmask, need);
+  emit(sm, n,
+       [&](int64_t i0, uint32_t* key, int32_t* pos) {
+         load4(s, i0, n, key);
+#pragma unroll
+         for (int j = 0; j < 4; j++) pos[j] = (int32_t)(i0 + j);
+       },
+       prefix, need, off, o, k);
+}
+
+// Positions of token t (lengths clamped to [0, ld]).
+__device__ __forceinline__ int64_t token_len(const int32_t* __restrict__ lengths, int64_t ld, int64_t t) {
+  const int64_t n = lengths ? (int64_t)lengths[t] : ld;
+  return n < 0 ? 0 : (n > ld ? ld : n);
+}
+
 __global__ __launch_bounds__(kThreadsK) void sparse_indexer_topk_kernel(const float* __restrict__ scores, int64_t ld,
                                                                        const int32_t* __restrict__ lengths,
                                                                        const int32_t* __restrict__ row_offset,
@@ -245,8 +407,7 @@ __global__ __launch_bounds__(kThreadsK) void sparse_indexer_topk_kernel(const fl
   __shared__ SmemTopk sm;
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
-  int64_t n = lengths ? (int64_t)lengths[t] : ld;
-  n = n < 0 ? 0 : (n > ld ? ld : n);
+  const int64_t n = token_len(lengths, ld, t);
   const int32_t off = row_offset ? row_offset[t] : 0;
   const float* s = scores + t * ld;
   int32_t* o = out + t * (int64_t)k;
@@ -261,10 +422,6 @@ __global__ __launch_bounds__(kThreadsK) void sparse_indexer_topk_kernel(const fl
   radix_step(sm, global_keys, 21, 2047u, prefix, pmask, need);
 
   const int64_t W = (n + 31) >> 5;   // bitmap words of the context
-  uint32_t cut = prefix >> 21;        // the chosen top-11-bit bin
-  // opaque to the optimizer, which would otherwise turn the sign-bit tests below back into
-  // compare-and-select pairs
-  asm volatile("" : "+v"(cut));
   uint32_t cnt = kCap + 1;
   if (W <= kMapWords) {
     // ---- pass 2: keys above the cut bin are in the list: set their bits; keys in the cut
@@ -274,127 +431,15 @@ __global__ __launch_bounds__(kThreadsK) void sparse_indexer_topk_kernel(const fl
       sm.tie[i] = 0;
     }
     __syncthreads();
-    const int wave = tid >> 6;
-    uint32_t wfill = 0;   // keys of the cut bin this wave found so far (uniform in the wave)
-    // one round.  The 4 positions of a 16-byte load share one bitmap word (they start at a
-    // multiple of 4), so each load sets its bits with one OR (of 0 when none is above the
-    // cut).  A lane's cut-bin keys go to its wave's region after those of lower lanes: the
-    // wave prefix sum of the counts (below 32) is built from ballots of their five bits.
-    auto round = [&](const uint32_t (&key)[4 * kVec], int64_t c, bool full) {
-      uint32_t cutm[kVec], m = 0;
-#pragma unroll
-      for (int j = 0; j < kVec; j++) {
-        const int64_t p = c + 4 * (tid + (int64_t)kThreadsK * j);
-        uint32_t am = 0, cm = 0;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          // bins are below 2^11: cut - b is negative exactly when b > cut, and
-          // (b ^ cut) - 1 exactly when b == cut
-          const uint32_t b = key[4 * j + e] >> 21;
-          uint32_t above = (cut - b) >> 31, equal = ((b ^ cut) - 1u) >> 31;
-          if (!full && p + e >= n) above = equal = 0;
-          am |= above << e;
-          cm |= equal << e;
-        }
-        if (p < n) atomicOr(&sm.above[p >> 5], am << (p & 31));
-        cutm[j] = cm;
-        m += __builtin_popcount(cm);
-      }
-      uint32_t before = 0, total = 0;
-#pragma unroll
-      for (int bit = 0; bit < 5; bit++) {
-        const uint64_t bal = __ballot((m >> bit) & 1u);
-        before += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))
-                  << bit;
-        total += (uint32_t)__popcll(bal) << bit;
-      }
-      if (m != 0) {
-        uint32_t i = wfill + before;
-#pragma unroll
-        for (int j = 0; j < kVec; j++) {
-          if (cutm[j] == 0) continue;
-          const int64_t p = c + 4 * (tid + (int64_t)kThreadsK * j);
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            if ((cutm[j] >> e) & 1u) {
-              if (i < (uint32_t)kCapWave) {
-                sm.ckey[wave * kCapWave + i] = key[4 * j + e];
-                sm.cpos[wave * kCapWave + i] = (int32_t)(p + e);
-              }
-              i++;
-            }
-          }
-        }
-      }
-      wfill += total;
-    };
-    for_rounds(s, n, round);
-    if ((tid & 63) == 0) sm.wcut[wave] = wfill;
-    __syncthreads();
+    classify_pass(sm, s, n, prefix >> 21);
     cnt = 0;
     for (int w = 0; w < kWavesK; w++) cnt = sm.wcut[w] > (uint32_t)kCapWave ? (uint32_t)kCap + 1 : cnt + sm.wcut[w];
   }
-
   if (cnt <= (uint32_t)kCap) {
-    // ---- the two remaining radix steps over the cut bin's keys, in LDS
     // entry i of the buffer holds a key when it lies below its wave's fill
-    auto kept = [&](int i) { return (uint32_t)(i % kCapWave) < sm.wcut[i / kCapWave]; };
-    auto lds_keys = [&](auto f) {
-      for (int i = tid; i < kCap; i += kThreadsK)
-        if (kept(i)) f(sm.ckey[i], (int64_t)0);
-    };
-    radix_step(sm, lds_keys, 10, 2047u, prefix, pmask, need);
-    radix_step(sm, lds_keys, 0, 1023u, prefix, pmask, need);
-    const uint32_t K = prefix;
-    for (int i = tid; i < kCap; i += kThreadsK) {
-      if (!kept(i)) continue;
-      const uint32_t key = sm.ckey[i];
-      const int32_t p = sm.cpos[i];
-      if (key > K) atomicOr(&sm.above[p >> 5], 1u << (p & 31));
-      else if (key == K) atomicOr(&sm.tie[p >> 5], 1u << (p & 31));
-    }
-    __syncthreads();
-    // ---- the list from the bitmaps: thread tid takes words [w0, w1); a set bit of `above`
-    // goes to gb + min(eb, need), one of `tie` to gb + eb while eb < need (gb / eb: bits of
-    // `above` / `tie` at lower positions)
-    const int per = (int)((W + kThreadsK - 1) / kThreadsK);
-    const int w0 = tid * per, w1 = (int)(w0 + per < W ? w0 + per : W);
-    uint32_t g = 0, e = 0;
-    for (int w = w0; w < w1; w++) {
-      g += __builtin_popcount(sm.above[w]);
-      e += __builtin_popcount(sm.tie[w]);
-    }
-    uint32_t tot;
-    uint32_t gb = block_scan(sm, g, tot) - g;
-    uint32_t eb = block_scan(sm, e, tot) - e;
-    for (int w = w0; w < w1; w++) {
-      const uint32_t a = sm.above[w], t = sm.tie[w];
-      uint32_t m = a | t;
-      while (m) {
-        const int bit = __builtin_ctz(m);
-        m &= m - 1;
-        const int32_t entry = off + (w * 32 + bit);
-        // the places are below k by construction; the test only keeps a write inside the row
-        if ((a >> bit) & 1u) {
-          const uint32_t place = gb + (eb < need ? eb : need);
-          if (place < (uint32_t)k) o[place] = entry;
-          gb++;
-        } else {
-          if (eb < need && gb + eb < (uint32_t)k) o[gb + eb] = entry;
-          eb++;
-        }
-      }
-    }
+    finish_in_lds(sm, [&](int i) { return (uint32_t)(i % kCapWave) < sm.wcut[i / kCapWave]; }, prefix, pmask,
+                  need, W, off, o, k);
   } else {
-    // ---- a long context or a crowded cut bin: the rest from the scores in memory
-    radix_step(sm, global_keys, 10, 2047u, prefix, pmask, need);
-    radix_step(sm, global_keys, 0, 1023u, prefix, pmask, need);
-    emit(sm, n,
-         [&](int64_t i0, uint32_t* key, int32_t* pos) {
-           load4(s, i0, n, key);
-#pragma unroll
-           for (int j = 0; j < 4; j++) pos[j] = (int32_t)(i0 + j);
-         },
-         prefix, need, off, o, k);
+    finish_in_memory(sm, s, n, prefix, pmask, need, off, o, k);
   }
 }

@@ -150,14 +150,32 @@ def test_fp8pool_entry_points_check_arguments(L):
 
 
 def test_indexer_entry_point_checks_arguments(L):
-    assert L.sparse_indexer_topk(None, 8, None, None, 0, 4, None, None) == 0           # T == 0: no-op
-    assert L.sparse_indexer_topk(P(16), 8, None, None, 2, 0, P(16), None) == -1        # k < 1
-    assert L.sparse_indexer_topk(P(16), 8, None, None, 2, 65537, P(16), None) == -1    # k too large
-    assert L.sparse_indexer_topk(P(16), 6, None, None, 2, 4, P(16), None) == -1        # ld not a multiple of 4
-    assert L.sparse_indexer_topk(P(8), 8, None, None, 2, 4, P(16), None) == -1         # misaligned scores
-    assert L.sparse_indexer_topk(None, 8, None, None, 2, 4, P(16), None) == -1
-    assert L.sparse_indexer_topk(P(16), 8, P(2), None, 2, 4, P(16), None) == -1        # misaligned lengths
-    assert L.sparse_indexer_topk(P(16), 8, None, None, 2, 4, None, None) == -1         # no output
+    def topk(scores=16, ld=8, lengths=None, T=2, k=4, out=16, parts=0, ws=None, nb=0):
+        return L.sparse_indexer_topk(P(scores), ld, P(lengths), None, T, k, P(out), parts, P(ws), nb, None)
+    assert topk(scores=None, out=None, T=0) == 0           # T == 0: no-op
+    assert topk(k=0) == -1                                 # k < 1
+    assert topk(k=65537) == -1                             # k too large
+    assert topk(ld=6) == -1                                # ld not a multiple of 4
+    assert topk(scores=8) == -1                            # misaligned scores
+    assert topk(scores=None) == -1
+    assert topk(lengths=2) == -1                           # misaligned lengths
+    assert topk(out=None) == -1                            # no output
+    assert topk(parts=-1) == -1
+    assert topk(parts=65) == -1                            # more workgroups per token than the split takes
+    assert topk(parts=2) == -3                             # a split without a workspace
+    assert topk(parts=2, ws=16, nb=16) == -3               # a workspace too small for it
+    assert topk(parts=2, ws=8, nb=1 << 30) == -3           # a misaligned one
+
+
+def test_indexer_workspace_query(L):
+    L.smla_indexer_workspace_bytes.restype = ctypes.c_size_t
+    assert L.smla_indexer_workspace_bytes(2, 8192, 4, 1) == 0          # one workgroup per token
+    two = L.smla_indexer_workspace_bytes(2, 8192, 4, 2)
+    assert two > 0 and two % 256 == 0
+    assert L.smla_indexer_workspace_bytes(2, 8192, 4, 7) > two         # a histogram per workgroup
+    assert L.smla_indexer_workspace_bytes(0, 8192, 4, 2) == 0
+    assert L.smla_indexer_workspace_bytes(2, 8192, 4, 65) == 0         # invalid
+    assert L.smla_indexer_workspace_bytes(2, 6, 4, 2) == 0
 
 
 def test_blhnc_entry_points_check_arguments(L):

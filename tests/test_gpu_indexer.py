@@ -173,3 +173,69 @@ def test_topk_many_tokens_long_context(smla):
     lengths[:3] = [S, 147457, 147456]
     got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), 2048, torch.from_numpy(lengths).to(DEV))
     assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, 2048))
+
+
+# Split selection: each token's positions over `parts` workgroups (histogram, classify and
+# finish launches), bit-exact against the same oracle, with chunk boundaries, empty chunks
+# (more workgroups than 32-position chunks), crowded cut bins (the finish from memory) and
+# contexts longer than the bitmaps.
+@pytest.mark.parametrize("kind", ["normal", "ties", "grid", "specials", "equal"])
+@pytest.mark.parametrize("parts", [2, 3, 7, 64])
+def test_topk_split_bit_exact(smla, kind, parts):
+    _say("topk split", kind, parts)
+    rng = np.random.default_rng(["normal", "ties", "grid", "specials", "equal"].index(kind) * 1000 + parts + 900)
+    T, S = 7, 20000
+    scores = _scores(kind, T, S, rng)
+    lengths = np.array([S, 0, 2047, 2049, 2048 + 33, 19999, 4096 + 64 * 31], dtype=np.int32)
+    off = rng.integers(0, 100000, size=T).astype(np.int32)
+    for k in (2048, 300, 1):
+        got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), k, torch.from_numpy(lengths).to(DEV),
+                                       torch.from_numpy(off).to(DEV), parts=parts)
+        ref = oracle.topk_indices_ref(scores, lengths, k, off)
+        assert np.array_equal(got.cpu().numpy(), ref), k
+
+
+@pytest.mark.parametrize("kind", ["equal", "three"])
+def test_topk_split_crowded_cut_bin(smla, kind):
+    rng = np.random.default_rng(51)
+    T, S = 3, 60000
+    scores = (np.full((T, S), 0.25, dtype=np.float32) if kind == "equal"
+              else rng.integers(0, 3, size=(T, S)).astype(np.float32))
+    lengths = np.array([S, 50001, 2049], dtype=np.int32)
+    for parts in (2, 9):
+        got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), 2048, torch.from_numpy(lengths).to(DEV),
+                                       parts=parts)
+        assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, 2048)), parts
+
+
+def test_topk_split_context_longer_than_the_bitmaps(smla):
+    rng = np.random.default_rng(52)
+    T, S = 3, 300000
+    scores = (np.round(rng.standard_normal((T, S)) * 64) / 64).astype(np.float32)
+    lengths = np.array([S, 147457, 147456], dtype=np.int32)
+    got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), 2048, torch.from_numpy(lengths).to(DEV),
+                                   parts=16)
+    assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, 2048))
+
+
+def test_topk_split_workspace_reuse(smla):
+    """One workspace, calls with other scores, lengths and k: the counters the split keeps in
+    it are left at zero for the next call."""
+    rng = np.random.default_rng(53)
+    T, S = 5, 40000
+    ws = smla.make_indexer_workspace(T, S, 2048, 5, DEV)
+    assert ws is not None
+    for i, kind in enumerate(["grid", "ties", "specials", "equal"]):
+        scores = _scores(kind, T, S, rng)
+        lengths = rng.integers(0, S + 1, size=T).astype(np.int32)
+        k = [2048, 700, 2048, 5][i]
+        got = smla.sparse_indexer_topk(torch.from_numpy(scores).to(DEV), k, torch.from_numpy(lengths).to(DEV),
+                                       parts=5, workspace=ws)
+        assert np.array_equal(got.cpu().numpy(), oracle.topk_indices_ref(scores, lengths, k)), kind
+
+
+def test_topk_automatic_split_is_used_for_few_tokens(smla):
+    """The 35-token workload's shape gets a workspace (a split) by default; the 264-token one
+    runs one workgroup per token."""
+    assert smla.indexer_workspace_bytes(35, 140000, 2048) > 0
+    assert smla.indexer_workspace_bytes(264, 146000, 2048) == 0
