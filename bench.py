@@ -29,7 +29,8 @@ and not the host): gathered KV bytes (352 per valid list entry) against 8 TB/s b
 the ridge (16 heads), matrix flops (2 * H * (576 + 512) per valid entry) against
 2.5 PFLOP/s above it (64 and 128 heads).  `cpu_baseline` times the CPU oracle on the
 host over a token sample of the headline workload.  Untimed for `value`, side legs
-report the staged two-pass variant, session-grouped decode, (`fp8_pool`) the same
+report the staged two-pass variant, session-grouped decode (only with --grouped K: on
+the 264-token workload it is slower than per-token decode), (`fp8_pool`) the same
 decode over the pool kept as 576-byte FP8 rows, the format NVFP4 replaces,
 (`indexer_topk`) the sparse indexer's top-2,048 selection that produces the lists,
 and (`block_major_pool`) decode and block transfer over the block-major multi-layer
@@ -685,9 +686,10 @@ def main():
     ap.add_argument("--check-tokens", type=int, default=3, help="tokens checked against the oracle (untimed)")
     ap.add_argument("--staged", type=int, default=20,
                     help="steps of the staged two-pass variant leg (the 1,024-token workload; 0 disables)")
-    ap.add_argument("--grouped", type=int, default=20,
+    ap.add_argument("--grouped", type=int, default=0,
                     help="steps of the session-grouped decode leg (union lists of groups of 64/H tokens, then "
-                         "one pass over them; the 264-token workload; 0 disables)")
+                         "one pass over them; the 264-token workload; off by default: there it is slower than "
+                         "per-token decode)")
     ap.add_argument("--fp8pool", type=int, default=50,
                     help="launches of decode over the same pool kept as 576-byte FP8 rows (the 264- and "
                          "1,024-token workloads; 0 disables)")

@@ -120,13 +120,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
       const uint32_t voff = ok ? (uint32_t)(cur.t * A.topk + k) * 4u : kOOB;
       if (ln < kWR) dma4(rs_idx, voff, lds_addr(idxbuf + ((i & 1) * kWaves + wid) * kWR));
     };
-    // DMA of this wave's rows of tile cur into ring slot i % 4 (its index entries must have
-    // landed); the portion's valid-row mask goes to sm.vmask.  Issued in step i-2: the slot
-    // last held tile i-4, accumulated in step i-3, before the barrier that ended it.
-    auto issue_rows = [&](const Cursor& cur, int i, int ln) {
+    // Index entry of this wave's row r16 of tile i (its DMA must have landed).
+    auto idx_entry = [&](int i, int ln) { return idxbuf[((i & 1) * kWaves + wid) * kWR + (ln & 15)]; };
+    // DMA of this wave's rows of tile cur into ring slot i % 4, e = the lane's index entry;
+    // the portion's valid-row mask goes to sm.vmask.  Issued in step i-2: the slot last held
+    // tile i-4, accumulated in step i-3, before the barrier that ended it.
+    auto issue_rows = [&](const Cursor& cur, int i, int ln, int32_t e) {
       const int r16 = ln & 15, g = ln >> 4;
       const int k = cur.ci * kTileRows + kWR * wid + r16;
-      const int32_t e = idxbuf[((i & 1) * kWaves + wid) * kWR + r16];
       const int32_t v = kGrouped ? (e < 0 ? -1 : (e & kRowMask)) : e;
       const bool ok = cur.c < c_hi && k < A.topk && row_valid(v, A.pool_rows);
       if (kGrouped && g == 0) sm.members[i % kST][kWR * wid + r16] = ok ? (uint8_t)(e >> kMemberShift) : 0;
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
     wait_vm<0>();
 #pragma unroll
     for (int d = 0; d < 2; d++) {
-      issue_rows(cr, d, lane);
+      issue_rows(cr, d, lane, idx_entry(d, lane));
       cr.next(cpt);
       issue_idx(cx, d + 2, lane);
       cx.next(cpt);
@@ -199,6 +200,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
             wait_vm<0>();
           }
         }
+
+        // LDS reads the step needs after QK^T, issued first so that QK^T covers their latency:
+        // the index entry of tile s+2 (landed by the last barrier; its slot is refilled by
+        // the DMA for tile s+4 issued later in this step) and the flags of tile s-1
+        const int32_t e_next = idx_entry(s + 2, ln);
+        const int pp = par ^ 1;
+        const int fl_prev = sm.wflag[pp][0] | sm.wflag[pp][1] | sm.wflag[pp][2] | sm.wflag[pp][3];
 
         // ---- QK^T: rows 16*MT*rg + 16m + r16 against heads 16*JT*hg + 16j + r16
         uint32_t vrow = 0;   // bit 16m + r: row 16*MT*rg + 16m + r is valid
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
         }
 
         // ---- rows of tile s+2, index entries of tile s+4 (issued behind the matrix work)
-        issue_rows(cr, s + 2, ln);
+        issue_rows(cr, s + 2, ln, e_next);
         cr.next(cpt);
         issue_idx(cx, s + 4, ln);
         cx.next(cpt);
@@ -282,9 +290,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
         // ---- shared references after tile s-1 of the same segment: the largest one the
         // row groups used
         if (s > 0 && !new_seg) {
-          const int pp = par ^ 1;
-          const int fl = sm.wflag[pp][0] | sm.wflag[pp][1] | sm.wflag[pp][2] | sm.wflag[pp][3];
-          if (fl & 1) {
+          if (fl_prev & 1) {
 #pragma unroll
             for (int j = 0; j < JT; j++) {
               const int h = 16 * JT * hg + 16 * j + r16;
