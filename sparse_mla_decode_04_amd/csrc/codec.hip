@@ -90,35 +90,64 @@ __global__ __launch_bounds__(256) void nvfp4_unpack_rows_kernel(const uint8_t* _
   }
 }
 
-// Staged pass 1: one wave per list entry; lane l re-encodes latent values 8l..8l+7 and
-// lanes 0..7 copy rope values 8l..8l+7 (already E4M3).  Empty entries write zeros.
+// Staged pass 1: sixteen lanes per list entry, four entries per wave, kStageRounds rounds of
+// entries per wave with every load of a round issued before any conversion.  Lane l of an
+// entry re-encodes latent groups l and 16 + l (two 8-byte code loads, two scale bytes) and
+// writes them as 16-byte stores at offsets 16l and 256 + 16l, so each store instruction
+// fills 256 contiguous bytes of the entry's output row; lanes 0..3 copy the rope (already
+// E4M3).  Empty entries write zeros.  The output is written with non-temporal stores: it
+// exceeds the caches and is read back only by the attention pass.
+constexpr int kStageRounds = 4;
+
 __global__ __launch_bounds__(256) void nvfp4_stage_fp8_kernel(const uint8_t* __restrict__ pool,
-                                                               int64_t pool_rows,
-                                                               const int32_t* __restrict__ idx,
-                                                               int64_t entries,
-                                                               uint8_t* __restrict__ staged) {
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t e = (int64_t)blockIdx.x * 4 + wid;
-  if (e >= entries) return;
-  const int32_t r = idx[e];
-  uint8_t* o = staged + e * kHeadDim;
-  if (!row_valid(r, pool_rows)) {
-    *(u32x2*)(o + 8 * lane) = u32x2{0, 0};
-    if (lane < 8) *(u32x2*)(o + kLatent + 8 * lane) = u32x2{0, 0};
-    return;
+                                                              int64_t pool_rows,
+                                                              const int32_t* __restrict__ idx,
+                                                              int64_t entries,
+                                                              uint8_t* __restrict__ staged) {
+  const int q = threadIdx.x >> 4, l = threadIdx.x & 15;
+  const int64_t e0 = (int64_t)blockIdx.x * (16 * kStageRounds) + q;
+  uint32_t code[kStageRounds][4], sc[kStageRounds][2];
+  u32x4 rope[kStageRounds];
+  bool ok[kStageRounds];
+#pragma unroll
+  for (int u = 0; u < kStageRounds; u++) {
+    const int64_t e = e0 + 16 * u;
+    const int32_t r = e < entries ? idx[e] : -1;
+    ok[u] = row_valid(r, pool_rows);
+    code[u][0] = code[u][1] = code[u][2] = code[u][3] = 0;
+    sc[u][0] = sc[u][1] = 0;
+    rope[u] = u32x4{0, 0, 0, 0};
+    if (ok[u]) {
+      const uint8_t* p = pool + (int64_t)r * kRowBytes;
+      const u32x2 a = *(const u32x2*)(p + 8 * l);
+      const u32x2 b = *(const u32x2*)(p + 128 + 8 * l);
+      code[u][0] = a.x;
+      code[u][1] = a.y;
+      code[u][2] = b.x;
+      code[u][3] = b.y;
+      sc[u][0] = p[kScaleOff + l];
+      sc[u][1] = p[kScaleOff + 16 + l];
+      if (l < 4) rope[u] = *(const u32x4*)(p + kRopeOff + 16 * l);
+    }
   }
-  const uint8_t* p = pool + (int64_t)r * kRowBytes;
-  const uint32_t w = *(const uint32_t*)(p + 4 * lane);
-  const uint32_t sc = p[kScaleOff + lane / 2];
-  const f16 s = e4m3x2<false>(sc).x;
-  const f16x8 v = unpack8(w, f16x2{s, s});
-  uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int k = 0; k < 4; k++) lo |= e4m3_encode_rne((float)v[k]) << (8 * k);
+  for (int u = 0; u < kStageRounds; u++) {
+    const int64_t e = e0 + 16 * u;
+    if (e >= entries) break;
+    uint8_t* o = staged + e * kHeadDim;
+    u32x4 v[2];
 #pragma unroll
-  for (int k = 0; k < 4; k++) hi |= e4m3_encode_rne((float)v[4 + k]) << (8 * k);
-  *(u32x2*)(o + 8 * lane) = u32x2{lo, hi};
-  if (lane < 8) *(u32x2*)(o + kLatent + 8 * lane) = *(const u32x2*)(p + kRopeOff + 8 * lane);
+    for (int h = 0; h < 2; h++) {
+      const f16 s = e4m3x2<false>(sc[u][h]).x;
+      const f16x8 lo = unpack8(code[u][2 * h], f16x2{s, s});
+      const f16x8 hi = unpack8(code[u][2 * h + 1], f16x2{s, s});
+      const u32x2 a = e4m3x8_sat(lo), b = e4m3x8_sat(hi);
+      v[h] = u32x4{a.x, a.y, b.x, b.y};
+    }
+    __builtin_nontemporal_store(v[0], (u32x4*)(o + 16 * l));
+    __builtin_nontemporal_store(v[1], (u32x4*)(o + 256 + 16 * l));
+    if (l < 4) __builtin_nontemporal_store(rope[u], (u32x4*)(o + kLatent + 16 * l));
+  }
 }
 
 // The 576-byte FP8 cache row (the format NVFP4 replaces in "Four-bit caches make room"):
@@ -174,7 +203,7 @@ hipError_t launch_unpack(const void* pool, int64_t pool_rows, const int32_t* row
 
 hipError_t launch_stage_fp8(const void* pool, int64_t pool_rows, const int32_t* idx,
                             int64_t entries, void* staged, hipStream_t s) {
-  const int64_t blocks = (entries + 3) / 4;
+  const int64_t blocks = (entries + 16 * kStageRounds - 1) / (16 * kStageRounds);
   hipLaunchKernelGGL(nvfp4_stage_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      (const uint8_t*)pool, pool_rows, idx, entries, (uint8_t*)staged);
   return hipGetLastError();

@@ -93,11 +93,6 @@ struct __attribute__((aligned(16))) Smem {
   int flag;
 };
 
-__device__ __forceinline__ u32x2 lds_read_tr8(const SMLA_LDS void* p) {
-  i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SMLA_LDS i32x2*)p);
-  return u32x2{(uint32_t)v.x, (uint32_t)v.y};
-}
-
 }  // namespace
 
 template <int NG, int ST, bool kFp8, int WPC>
@@ -471,6 +466,7 @@ hipError_t launch_decode_nvfp4(const DecodeArgs& a, hipStream_t s, int variant) 
 hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t s) { return launch_decode_nvfp4_ws(a, s, 64, true); }
 
 hipError_t launch_decode_fp8rows(const DecodeArgs& a, hipStream_t s) {
+  if (a.HB * 4 * kHeadGroup == a.H) return launch_decode_fp8_ws(a, s);
   return (a.HB * 2 * kHeadGroup == a.H) ? launch_variant<2, 2, true, 1>(a, s)
                                         : launch_variant<1, 2, true, 1>(a, s);
 }

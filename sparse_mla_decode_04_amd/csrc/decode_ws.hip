@@ -31,6 +31,14 @@
 //    the group scales) feeds NH/16 pairs of MFMAs.
 //  * Split epilogue as in the other kernels; the in-launch merge runs as two teams of four
 //    waves (NH = 64: 32 heads each; NH = 16: the first team, the second joins its barriers).
+//
+// With kFp8 (NH = 64) the kernel attends over 576-byte FP8 E4M3 rows instead: the rows
+// pass 1 of the staged variant wrote to HBM (one per list entry) or the rows of a pool kept
+// in FP8.  E4M3 -> fp16 is exact and takes one conversion per pair of values, with no group
+// scales; PV reads V^T through the 8-bit LDS transpose read.  The 512-byte latent goes to
+// the four-slot ring and the 64-byte rope to a three-slot ring of its own: only QK^T reads
+// the rope, in the step that scores the tile, and a four-slot ring of whole rows would not
+// leave room in LDS for the probability tables.
 #include "smla_launch.hpp"
 #include "smla_tile.hpp"
 
@@ -38,12 +46,24 @@ namespace smla {
 
 namespace {
 
-constexpr int kPieces = kRowBytes / 16;   // 22
-constexpr int kLoads = 6;                 // DMA instructions per scoring wave per tile (pieces 0..23)
-constexpr int kPortion = kPieces * 256;   // one scoring wave's 16 rows, [piece][row]
-constexpr int kSlot = kWaves * kPortion;  // one tile
 constexpr int kST = 4;                    // ring slots
 constexpr int kThreads = 2 * kWaves * 64; // scoring waves 0..3, accumulating waves 4..7
+
+// Ring layout of a row format.  NVFP4: the whole 352-byte row in the ring (pieces 0..15
+// codes, 16..17 scales, 18..21 rope).  FP8: the latent (pieces 0..31) in the ring, the rope
+// in the rope ring.
+template <bool kFp8>
+struct WsFmt {
+  static constexpr int kPieces = kFp8 ? kLatent / 16 : kRowBytes / 16;   // 32 or 22
+  static constexpr int kLoads = (kPieces + 3) / 4;     // ring DMA per scoring wave per tile: 8 or 6
+  static constexpr int kPortion = kPieces * 256;       // one scoring wave's 16 rows, [piece][row]
+  static constexpr int kSlot = kWaves * kPortion;      // one tile
+  static constexpr int kRopeST = kFp8 ? 3 : 0;         // rope ring slots
+  static constexpr int kRopePortion = 4 * 256;         // 16 rows x 4 pieces of rope
+  static constexpr int kRopeSlot = kWaves * kRopePortion;
+  static constexpr int kVmOps = kLoads + (kFp8 ? 1 : 0);   // vector memory instructions per tile
+  static constexpr int kRingBytes = kST * kSlot + kRopeST * kRopeSlot;
+};
 
 template <int NH>
 struct WsShape {
@@ -55,12 +75,13 @@ struct WsShape {
   static constexpr int NJ = NH / 16;            // 16-head tiles of an accumulating wave
 };
 
-template <int NH>
+template <int NH, bool kGrouped, bool kFp8>
 struct __attribute__((aligned(16))) SmemWs {
-  uint8_t ring[kST][kSlot];               // [slot][portion][piece][row] 16-byte pieces
-  uint8_t members[kST][kTileRows];        // grouped decode: member bits of each row [slot][row]
+  // [slot][portion][piece][row] 16-byte pieces, then (FP8) the rope ring [slot][portion][piece][row]
+  uint8_t ring[WsFmt<kFp8>::kRingBytes];
+  uint8_t members[(kGrouped || !kFp8) ? kST : 1][kTileRows];   // grouped decode: member bits [slot][row]
   int32_t idx[2][kWaves][kWR];            // index-list DMA landing zone [tile parity][portion]
-  f16 sc[2][32][kPH];                     // PV scales [parity][group][tile row]
+  f16 sc[2][kFp8 ? 1 : 32][kPH];          // NVFP4 PV scales [parity][group][tile row]
   f16 pb[2][NH][kPH];                     // probabilities [parity][head][tile row]
   float wref[2][WsShape<NH>::RG][NH];     // reference each row group used [parity][group][head]
   int wflag[2][kWaves];                   // bit 0: wave raised a reference; bit 1: wave has a row
@@ -81,12 +102,14 @@ __device__ __forceinline__ int fresh_lane(int lane) {
 // kGrouped: the index entries are union-list entries of token groups (row | members << 27),
 // the NH = 64 heads are those of the group's tokens (A.tok_heads heads each), and a score
 // counts only where the head's token lists the row.
-template <int NH, bool kGrouped>
+template <int NH, bool kGrouped, bool kFp8>
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(DecodeArgs A) {
   using S = WsShape<NH>;
+  using F = WsFmt<kFp8>;
   constexpr int JT = S::JT, RG = S::RG, MT = S::MT, NJ = S::NJ;
-  static_assert(sizeof(SmemWs<NH>) <= 160 * 1024, "LDS of one CU");
-  __shared__ SmemWs<NH> sm;
+  static_assert(!kFp8 || (NH == 64 && !kGrouped), "FP8 rows: 64-head blocks, per-token lists");
+  static_assert(sizeof(SmemWs<NH, kGrouped, kFp8>) <= 160 * 1024, "LDS of one CU");
+  __shared__ SmemWs<NH, kGrouped, kFp8> sm;
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -102,6 +125,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
   const int n = (int)(c_hi - c_lo);
   const int head0 = hb * NH;
   SMLA_LDS uint8_t* const ring = (SMLA_LDS uint8_t*)sm.ring;
+  SMLA_LDS uint8_t* const rope_ring = ring + kST * F::kSlot;   // FP8 only
   const __amdgpu_buffer_rsrc_t ws_o = merge_rsrc(A.part_o, A.part_o_bytes);
   const __amdgpu_buffer_rsrc_t ws_l = merge_rsrc(A.part_lse, A.part_lse_bytes);
 
@@ -122,22 +146,29 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
     };
     // Index entry of this wave's row r16 of tile i (its DMA must have landed).
     auto idx_entry = [&](int i, int ln) { return idxbuf[((i & 1) * kWaves + wid) * kWR + (ln & 15)]; };
-    // DMA of this wave's rows of tile cur into ring slot i % 4, e = the lane's index entry;
-    // the portion's valid-row mask goes to sm.vmask.  Issued in step i-2: the slot last held
-    // tile i-4, accumulated in step i-3, before the barrier that ended it.
+    // DMA of this wave's rows of tile cur into ring slot i % 4 (FP8: and their rope into
+    // rope slot i % 3), e = the lane's index entry; the portion's valid-row mask goes to
+    // sm.vmask.  Issued in step i-2: the slot last held tile i-4, accumulated in step i-3,
+    // before the barrier that ended it (the rope slot: tile i-3, scored in step i-3).
     auto issue_rows = [&](const Cursor& cur, int i, int ln, int32_t e) {
       const int r16 = ln & 15, g = ln >> 4;
       const int k = cur.ci * kTileRows + kWR * wid + r16;
       const int32_t v = kGrouped ? (e < 0 ? -1 : (e & kRowMask)) : e;
       const bool ok = cur.c < c_hi && k < A.topk && row_valid(v, A.pool_rows);
       if (kGrouped && g == 0) sm.members[i % kST][kWR * wid + r16] = ok ? (uint8_t)(e >> kMemberShift) : 0;
-      const uint32_t base = storage_row((uint32_t)v, A.map) * (uint32_t)kRowBytes;
-      const uint32_t lds0 = lds_addr(ring + (i % kST) * kSlot + wid * kPortion);
+      // FP8: row v of a pool, or the staged row of entry (t, k)
+      const uint32_t base = kFp8 ? (uint32_t)(A.fp8_pool ? (int64_t)v : cur.t * A.topk + k) * (uint32_t)kHeadDim
+                                 : storage_row((uint32_t)v, A.map) * (uint32_t)kRowBytes;
+      const uint32_t lds0 = lds_addr(ring + (i % kST) * F::kSlot + wid * F::kPortion);
 #pragma unroll
-      for (int kk = 0; kk < kLoads; kk++) {
+      for (int kk = 0; kk < F::kLoads; kk++) {
         const int piece = 4 * kk + g;
         const uint32_t voff = ok ? base + 16u * piece : kOOB;
-        if (4 * kk + 3 < kPieces || piece < kPieces) dma16(rs_rows, voff, lds0 + 1024u * kk);
+        if (4 * kk + 3 < F::kPieces || piece < F::kPieces) dma16(rs_rows, voff, lds0 + 1024u * kk);
+      }
+      if constexpr (kFp8) {
+        const uint32_t voff = ok ? base + (uint32_t)kLatent + 16u * g : kOOB;
+        dma16(rs_rows, voff, lds_addr(rope_ring + (i % F::kRopeST) * F::kRopeSlot + wid * F::kRopePortion));
       }
       const uint32_t vm = (uint32_t)__ballot(ok && g == 0) & 0xFFFFu;
       if (ln == 0) sm.vmask[i % kST][wid] = vm;
@@ -178,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
       issue_idx(cx, d + 2, lane);
       cx.next(cpt);
     }
-    wait_vm<kLoads + 1>();   // rows(0), idx(2) have landed
+    wait_vm<F::kVmOps + 1>();   // rows(0), idx(2) have landed
     __syncthreads();         // every portion of tile 0 has landed
 
     float mq[JT];   // shared reference of head 16*JT*hg + 16j + r16
@@ -187,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
     for (int s = 0; s <= n; s++) {
       if (s < n) {
         const int par = s & 1;
-        const SMLA_LDS uint8_t* const slot = ring + (s % kST) * kSlot;
+        const SMLA_LDS uint8_t* const slot = ring + (s % kST) * F::kSlot;
         const int ln = fresh_lane(lane), r16 = ln & 15, g = ln >> 4;
         const bool new_seg = cu.ci == 0;
         if (new_seg) {
@@ -225,10 +256,40 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
 #pragma unroll
           for (int j = 0; j < JT; j++) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         f16x2 sp[MT][4];   // group scales of the lane's rows: sp[m][q] = groups 8g+2q, 8g+2q+1
-        if (vrow != 0) {
+        if (kFp8 && vrow != 0) {
+          // FP8: K step k reads latent features 128g + 8k .. +7 of the row: 16-byte piece
+          // 8g + k/2, half k%2
+#pragma unroll
+          for (int kp = 0; kp < 8; kp++) {
+            u32x4 cw[MT];
+#pragma unroll
+            for (int m = 0; m < MT; m++)
+              cw[m] = lds_load<u32x4>(slot + (MT * rg + m) * F::kPortion + 256 * (8 * g + kp) + 16 * r16);
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++) {
+#pragma unroll
+              for (int m = 0; m < MT; m++) {
+                const f16x8 a = fp8x8(cw[m][2 * kk], cw[m][2 * kk + 1]);
+#pragma unroll
+                for (int j = 0; j < JT; j++) acc[m][j] = mfma16x16x32(a, Q[j][2 * kp + kk], acc[m][j]);
+              }
+            }
+          }
+          const SMLA_LDS uint8_t* const rslot = rope_ring + (s % F::kRopeST) * F::kRopeSlot;
 #pragma unroll
           for (int m = 0; m < MT; m++) {
-            const SMLA_LDS uint8_t* por = slot + (MT * rg + m) * kPortion + 16 * r16;
+            const u32x4 rb = lds_load<u32x4>(rslot + (MT * rg + m) * F::kRopePortion + 256 * g + 16 * r16);
+            const f16x8 r0 = fp8x8(rb.x, rb.y), r1 = fp8x8(rb.z, rb.w);
+#pragma unroll
+            for (int j = 0; j < JT; j++) {
+              acc[m][j] = mfma16x16x32(r0, Q[j][16], acc[m][j]);
+              acc[m][j] = mfma16x16x32(r1, Q[j][17], acc[m][j]);
+            }
+          }
+        } else if (!kFp8 && vrow != 0) {
+#pragma unroll
+          for (int m = 0; m < MT; m++) {
+            const SMLA_LDS uint8_t* por = slot + (MT * rg + m) * F::kPortion + 16 * r16;
             const u32x2 scb = lds_load<u32x2>(por + 256 * (16 + (g >> 1)) + 8 * (g & 1));
             sp[m][0] = e4m3x2<false>(scb.x);
             sp[m][1] = e4m3x2<true>(scb.x);
@@ -240,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
             u32x4 cw[MT];
 #pragma unroll
             for (int m = 0; m < MT; m++)
-              cw[m] = lds_load<u32x4>(slot + (MT * rg + m) * kPortion + 256 * (4 * g + kq) + 16 * r16);
+              cw[m] = lds_load<u32x4>(slot + (MT * rg + m) * F::kPortion + 256 * (4 * g + kq) + 16 * r16);
 #pragma unroll
             for (int kk = 0; kk < 4; kk++) {
               const int k = 4 * kq + kk;
@@ -255,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
           }
 #pragma unroll
           for (int m = 0; m < MT; m++) {
-            const u32x4 rb = lds_load<u32x4>(slot + (MT * rg + m) * kPortion + 256 * (18 + g) + 16 * r16);
+            const u32x4 rb = lds_load<u32x4>(slot + (MT * rg + m) * F::kPortion + 256 * (18 + g) + 16 * r16);
             const f16x8 r0 = fp8x8(rb.x, rb.y), r1 = fp8x8(rb.z, rb.w);
 #pragma unroll
             for (int j = 0; j < JT; j++) {
@@ -271,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
         }
         // PV scale table: the head-group-0 waves write their rows' scales (an empty row was
         // fetched as zeros, so its scales are 0)
-        if (hg == 0) {
+        if (!kFp8 && hg == 0) {
 #pragma unroll
           for (int m = 0; m < MT; m++) {
             const int row = 16 * MT * rg + 16 * m + r16;
@@ -348,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
         const bool wave_raised = __ballot(raised) != 0;
         sm.wflag[par][wid] = (wave_raised ? 1 : 0) | (vrow != 0 ? 2 : 0);
         cu.next(cpt);
-        wait_vm<kLoads + 1>();   // rows(s+1), idx(s+3) have landed
+        wait_vm<F::kVmOps + 1>();   // rows(s+1), idx(s+3) have landed
       }
       __syncthreads();
     }
@@ -374,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
     for (int s = 0; s <= n; s++) {
       if (s > 0) {
         const int par = (s - 1) & 1;
-        const SMLA_LDS uint8_t* const slot = ring + ((s - 1) % kST) * kSlot;
+        const SMLA_LDS uint8_t* const slot = ring + ((s - 1) % kST) * F::kSlot;
         const int ln = fresh_lane(lane), r16 = ln & 15, g = ln >> 4;
         // ---- PV operand: probabilities of all NH heads, rows 8g..8g+7 (half 0) and
         // 32+8g.. (half 1); those rows belong to row group rgh[half]
@@ -420,9 +481,27 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
         // 4-bit transpose read: lane s of group g supplies tile row 8g+s (s < 8) or
         // 32+8g+s-8; dword 0 then holds rows 8g..8g+7 and dword 1 rows 32+8g.. of feature
         // 16*tau + r16.
-        if (fl & 2) {
+        if (kFp8 && (fl & 2)) {
+          // 8-bit transpose read: lane s of group g supplies 8 bytes of tile row 8g + s/2
+          // (a0) or 32 + 8g + s/2 (a1) at feature offset 8*(s%2) of piece tau; lane i
+          // receives feature 16*tau + i of the group's 8 rows.
+          const int R0 = 8 * g + (r16 >> 1), R1 = R0 + 32;
+          const SMLA_LDS uint8_t* tb0 = slot + (R0 >> 4) * F::kPortion + 16 * (R0 & 15) + 8 * (r16 & 1) + 2048 * pw;
+          const SMLA_LDS uint8_t* tb1 = slot + (R1 >> 4) * F::kPortion + 16 * (R1 & 15) + 8 * (r16 & 1) + 2048 * pw;
+#pragma unroll
+          for (int k = 0; k < 8; k++) {
+            const u32x2 d0 = lds_read_tr8(tb0 + 256 * k);
+            const u32x2 d1 = lds_read_tr8(tb1 + 256 * k);
+            const f16x8 a0 = fp8x8(d0.x, d0.y), a1 = fp8x8(d1.x, d1.y);
+#pragma unroll
+            for (int j4 = 0; j4 < NJ; j4++) {
+              O[k][j4] = mfma16x16x32(a0, bop[j4][0], O[k][j4]);
+              O[k][j4] = mfma16x16x32(a1, bop[j4][1], O[k][j4]);
+            }
+          }
+        } else if (!kFp8 && (fl & 2)) {
           const int R = (r16 < 8) ? (8 * g + r16) : (32 + 8 * g + r16 - 8);
-          const SMLA_LDS uint8_t* tb = slot + (R >> 4) * kPortion + 16 * (R & 15) + 1024 * pw;
+          const SMLA_LDS uint8_t* tb = slot + (R >> 4) * F::kPortion + 16 * (R & 15) + 1024 * pw;
 #pragma unroll
           for (int k = 0; k < 8; k++) {
             const int tau = 8 * pw + k;
@@ -532,11 +611,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
 hipError_t launch_decode_nvfp4_ws(const DecodeArgs& a, hipStream_t s, int heads, bool grouped) {
   const dim3 grid(a.G * a.HB), block(kThreads);
   if (grouped)
-    hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<64, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<64, true, false>), grid, block, 0, s, a);
   else if (heads == 64)
-    hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<64, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<64, false, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<16, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<16, false, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fp8_ws(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((sparse_mla_decode_ws_kernel<64, false, true>), dim3(a.G * a.HB), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

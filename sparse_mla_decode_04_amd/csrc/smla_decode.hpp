@@ -104,7 +104,7 @@ __host__ __device__ inline int64_t wg_of_chunk(int64_t c, int64_t C, int64_t G) 
 inline int32_t heads_per_block_groups(int32_t H, int32_t topk, bool fp8rows, bool grouped = false) {
   if (grouped) return 4;
   if (topk <= kTileRows) return 1;
-  if (!fp8rows && H % (4 * kHeadGroup) == 0) return 4;
+  if (H % (4 * kHeadGroup) == 0) return 4;
   return H % (2 * kHeadGroup) == 0 ? 2 : 1;
 }
 

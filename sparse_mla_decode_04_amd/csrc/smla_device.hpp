@@ -107,6 +107,25 @@ __device__ __forceinline__ f16x8 fp8x8(uint32_t lo, uint32_t hi) {
   return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// Four fp16 values -> four E4M3 codes in one dword (value k in byte k): nearest, ties to
+// the even code, saturating at +-448, sign kept.  The gfx950 conversion (scale 1) rounds
+// to nearest even; clamping to the largest finite E4M3 magnitude first gives the
+// saturation, since no clamped value lies past 448.
+__device__ __forceinline__ uint32_t e4m3x4_sat(f16x2 a, f16x2 b) {
+  const f16x2 lo = f16x2{(f16)-448.0f, (f16)-448.0f}, hi = f16x2{(f16)448.0f, (f16)448.0f};
+  a = __builtin_elementwise_min(__builtin_elementwise_max(a, lo), hi);
+  b = __builtin_elementwise_min(__builtin_elementwise_max(b, lo), hi);
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  s16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, a, 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, b, 1.0f, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+// Eight fp16 values -> eight E4M3 codes in two dwords (as e4m3x4_sat).
+__device__ __forceinline__ u32x2 e4m3x8_sat(f16x8 v) {
+  return u32x2{e4m3x4_sat(f16x2{v[0], v[1]}, f16x2{v[2], v[3]}), e4m3x4_sat(f16x2{v[4], v[5]}, f16x2{v[6], v[7]})};
+}
+
 // ------------------------------------------------------------------ matrix cores --
 // D = A(16x32) * B(32x16) + C with fp16 operands and fp32 accumulation.  Lane l holds
 // A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16], and C/D[4*(l/16) .. +3][l%16].
@@ -119,6 +138,14 @@ __device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
 // group, lane s's nibble landing at nibble position s of the result.
 __device__ __forceinline__ u32x2 lds_read_tr4(const SMLA_LDS void* p) {
   i32x2 v = __builtin_amdgcn_ds_read_tr4_b64_v2i32((SMLA_LDS i32x2*)p);
+  return u32x2{(uint32_t)v.x, (uint32_t)v.y};
+}
+
+// LDS transpose read of 8-bit elements: within each group of 16 lanes, the 8-byte chunks
+// the lanes address, in lane order, form a row-major 8 x 16 byte matrix (lanes 2r and
+// 2r+1 make row r); lane i receives column i, row r in byte r.
+__device__ __forceinline__ u32x2 lds_read_tr8(const SMLA_LDS void* p) {
+  i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SMLA_LDS i32x2*)p);
   return u32x2{(uint32_t)v.x, (uint32_t)v.y};
 }
 

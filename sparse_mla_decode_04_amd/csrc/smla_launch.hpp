@@ -30,7 +30,10 @@ hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t s);
 // Union lists of token groups (group.hip).
 hipError_t launch_group_union(const int32_t* idx, int32_t T, int32_t topk, int32_t tpg, int64_t pool_rows,
                               int32_t U, int32_t* uni, int32_t* count, hipStream_t s);
+// Decode over FP8 rows (staged rows or an FP8 pool): 64-head blocks use the
+// role-specialised kernel, 32- and 16-head blocks the LDS-ring kernel.
 hipError_t launch_decode_fp8rows(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_fp8_ws(const DecodeArgs& a, hipStream_t s);
 // Copies n segments of seg_bytes (a multiple of 16) from src segment src_ids[i] to dst
 // segment dst_ids[i] (layout.hip); a null id array means segment i.
 hipError_t launch_copy_segments(const void* src, int64_t src_segs, const int32_t* src_ids, void* dst,

@@ -2,7 +2,7 @@
 CPU oracle: the row writer fp8_pack_rows bit-exact against oracle.fp8_pack_rows_ref,
 and sparse_mla_decode_fp8pool within the decode tolerance (max |out - ref| <= 2e-3
 max |ref|, |lse - ref| <= 1e-3, -inf exactly where the oracle has it) against
-oracle.sparse_mla_decode_fp8pool_ref: head blocks of 16 and 32, several tiles with a
+oracle.sparse_mla_decode_fp8pool_ref: head blocks of 16, 32 and 64, several tiles with a
 ragged tail, empty and out-of-range entries, empty tokens, every kind of split; and at
 the full sizes of the 35- and 264-token workloads on sampled tokens."""
 
@@ -72,6 +72,11 @@ def test_fp8_pack_bit_exact(smla):
     (2, 128, 3000, 300, 0.3, 5),
     (9, 16, 2000, 1, 0.0, 0),         # a single entry per token
     (4, 48, 2500, 130, 0.0, 3),       # 16-head blocks
+    (5, 64, 4000, 700, 0.1, 0),       # 64-head blocks: the role-specialised kernel, ragged tail
+    (5, 64, 4000, 700, 0.1, 3),       # ranges across tokens
+    (3, 128, 3000, 1000, 0.3, 7),
+    (2, 64, 3000, 2048, 0.0, 1000),   # one tile per workgroup
+    (3, 192, 3000, 256, 0.2, 0),      # three 64-head blocks
 ])
 def test_fp8pool_decode_matches_oracle(smla, T, H, N, K, empty_frac, splits):
     _say("fp8pool decode", T, H, N, K, empty_frac, splits)

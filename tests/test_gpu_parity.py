@@ -106,18 +106,25 @@ def test_unpack_all_code_scale_pairs_bit_exact(smla):
     assert np.all(got[:2].view(np.uint16) == 0) and np.all(got[258:].view(np.uint16) == 0)
 
 
-def test_stage_fp8_bit_exact(smla):
-    rng = np.random.default_rng(5)
+@pytest.mark.parametrize("T,K", [(3, 100), (1, 37), (5, 1021)])
+def test_stage_fp8_bit_exact(smla, T, K):
+    rng = np.random.default_rng(5 + T)
     src = _edge_rows(rng, 300)
     src[3:5] = rng.standard_normal((2, 576)).astype(np.float16)   # keep staged values < 448
+    # group scales around the E4M3 subnormal range: staged values land on the subnormal grid
+    src[6:60] = (rng.standard_normal((54, 576)) * rng.choice([0.004, 0.01, 0.02, 0.05], size=(54, 1))
+                 ).astype(np.float16)
     rows = oracle.nvfp4_pack_rows_ref(src)
-    idx = rng.integers(-1, 300, size=(3, 100)).astype(np.int32)
+    idx = rng.integers(-1, 310, size=(T, K)).astype(np.int32)      # ids >= 300 lie outside the pool
+    _say("stage: T", T, "K", K)
     staged = _np(smla.nvfp4_stage_fp8(torch.from_numpy(rows).to(DEV), torch.from_numpy(idx).to(DEV)))
-    for t in range(3):
-        for j in range(100):
-            r = idx[t, j]
-            exp = oracle.fp8_stage_rows_ref(rows[r:r + 1])[0] if r >= 0 else np.zeros(576, np.uint8)
-            assert np.array_equal(staged[t, j], exp), (t, j, r)
+    ref = oracle.fp8_stage_rows_ref(rows)
+    valid = (idx >= 0) & (idx < 300)
+    exp = np.where(valid[..., None], ref[np.where(valid, idx, 0)], np.uint8(0))
+    bad = np.argwhere(np.any(staged != exp, axis=2))
+    assert bad.size == 0, f"{len(bad)} entries differ, first (t, j) = {tuple(bad[0])}, row {idx[tuple(bad[0])]}"
+    mag = ref[6:60] & 0x7F
+    assert ((mag > 0) & (mag < 8)).any()   # subnormal E4M3 codes occur
 
 
 # ----------------------------------------------------------------------------- decode
@@ -303,11 +310,20 @@ def test_combine_matches_oracle(smla):
 
 # ----------------------------------------------------------------------------- staged variant
 
-def test_staged_variant_matches_staged_oracle(smla):
-    wl, src, q, idx = _setup(4, 16, 3000, 1000, 0.1, 22)
+@pytest.mark.parametrize("T,H,K,ef,splits", [
+    (4, 16, 1000, 0.1, 0),
+    (4, 64, 1000, 0.1, 0),     # 64-head blocks: the role-specialised kernel
+    (5, 64, 700, 0.2, 3),      # ragged last tile, ranges across tokens
+    (3, 128, 2048, 0.05, 0),
+    (2, 192, 300, 0.3, 1000),  # three head blocks, one tile per workgroup
+])
+def test_staged_variant_matches_staged_oracle(smla, T, H, K, ef, splits):
+    _say("staged", T, H, K, ef, splits)
+    wl, src, q, idx = _setup(T, H, 3000, K, ef, 22 + H + splits)
     pool = build_device_pool(src, DEV)
     idd = torch.from_numpy(idx).to(DEV)
     staged = smla.nvfp4_stage_fp8(pool, idd)
-    out, lse = smla.sparse_mla_decode_fp8rows(torch.from_numpy(q).to(DEV), staged, idd, 3000, wl.softmax_scale)
+    out, lse = smla.sparse_mla_decode_fp8rows(torch.from_numpy(q).to(DEV), staged, idd, 3000, wl.softmax_scale,
+                                              num_splits=splits)
     ref_o, ref_l = oracle.sparse_mla_decode_fp8rows_ref(q, OracleRows(src), idx, wl.softmax_scale)
-    assert_parity(_np(out), _np(lse), ref_o, ref_l, "staged")
+    assert_parity(_np(out), _np(lse), ref_o, ref_l, f"staged T{T} H{H} K{K} splits {splits}")

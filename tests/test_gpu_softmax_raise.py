@@ -164,7 +164,7 @@ def test_variant_later_tiles_dominate(variant):
 
 
 @pytest.mark.parametrize("kind", ["ramp", "wide"])
-@pytest.mark.parametrize("H", [16, 32])
+@pytest.mark.parametrize("H", [16, 32, 64, 128])
 def test_fp8pool_later_tiles_dominate(smla, kind, H):
     src, q, idx, scale = (ramp_inputs if kind == "ramp" else wide_inputs)(3, H, 5000, 2048, 340 + H)
     pool = build_device_fp8_pool(src, DEV)
@@ -177,17 +177,18 @@ def test_fp8pool_later_tiles_dominate(smla, kind, H):
 
 
 @pytest.mark.parametrize("kind", ["ramp", "wide"])
-def test_staged_later_tiles_dominate(smla, kind):
-    src, q, idx, scale = (ramp_inputs if kind == "ramp" else wide_inputs)(3, 16, 5000, 2048, 350)
+@pytest.mark.parametrize("H", [16, 64])
+def test_staged_later_tiles_dominate(smla, kind, H):
+    src, q, idx, scale = (ramp_inputs if kind == "ramp" else wide_inputs)(3, H, 5000, 2048, 350 + H)
     pool = build_device_pool(src, DEV)
     idd = torch.from_numpy(idx).to(DEV)
     staged = smla.nvfp4_stage_fp8(pool, idd)
     ref_o, ref_l = oracle.sparse_mla_decode_fp8rows_ref(q, OracleRows(src), idx, scale)
     for splits in (1, 4, 0):
-        _say("staged raise", kind, splits)
+        _say("staged raise", kind, H, splits)
         out, lse = smla.sparse_mla_decode_fp8rows(torch.from_numpy(q).to(DEV), staged, idd, 5000, scale,
                                                   num_splits=splits)
-        assert_parity(_np(out), _np(lse), ref_o, ref_l, f"staged {kind} splits {splits}")
+        assert_parity(_np(out), _np(lse), ref_o, ref_l, f"staged {kind} H{H} splits {splits}")
 
 
 @pytest.mark.parametrize("splits", [1, 3, 0])
