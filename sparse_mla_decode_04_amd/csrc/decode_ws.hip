@@ -147,10 +147,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
     // Index entry of this wave's row r16 of tile i (its DMA must have landed).
     auto idx_entry = [&](int i, int ln) { return idxbuf[((i & 1) * kWaves + wid) * kWR + (ln & 15)]; };
     // DMA of this wave's rows of tile cur into ring slot i % 4 (FP8: and their rope into
-    // rope slot i % 3), e = the lane's index entry; the portion's valid-row mask goes to
-    // sm.vmask.  Issued in step i-2: the slot last held tile i-4, accumulated in step i-3,
-    // before the barrier that ended it (the rope slot: tile i-3, scored in step i-3).
-    auto issue_rows = [&](const Cursor& cur, int i, int ln, int32_t e) {
+    // rope slot i % 3), e = the lane's index entry.  Issued in step i-2: the slot last held
+    // tile i-4, accumulated in step i-3, before the barrier that ended it (the rope slot:
+    // tile i-3, scored in step i-3).  prep_rows takes the lane's row address and writes the
+    // portion's valid-row mask to sm.vmask (and, grouped, the member bits);
+    // row_dma(rd, d) issues DMA instruction d of the F::kVmOps (ring pieces 4d .. 4d+3; FP8
+    // d = F::kLoads: the rope).
+    struct RowDma {
+      uint32_t base;   // byte offset of the lane's row (unused where !ok)
+      bool ok;
+      int slot;        // tile i
+    };
+    auto prep_rows = [&](const Cursor& cur, int i, int ln, int32_t e) -> RowDma {
       const int r16 = ln & 15, g = ln >> 4;
       const int k = cur.ci * kTileRows + kWR * wid + r16;
       const int32_t v = kGrouped ? (e < 0 ? -1 : (e & kRowMask)) : e;
@@ -159,19 +167,26 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
       // FP8: row v of a pool, or the staged row of entry (t, k)
       const uint32_t base = kFp8 ? (uint32_t)(A.fp8_pool ? (int64_t)v : cur.t * A.topk + k) * (uint32_t)kHeadDim
                                  : storage_row((uint32_t)v, A.map) * (uint32_t)kRowBytes;
-      const uint32_t lds0 = lds_addr(ring + (i % kST) * F::kSlot + wid * F::kPortion);
-#pragma unroll
-      for (int kk = 0; kk < F::kLoads; kk++) {
-        const int piece = 4 * kk + g;
-        const uint32_t voff = ok ? base + 16u * piece : kOOB;
-        if (4 * kk + 3 < F::kPieces || piece < F::kPieces) dma16(rs_rows, voff, lds0 + 1024u * kk);
-      }
-      if constexpr (kFp8) {
-        const uint32_t voff = ok ? base + (uint32_t)kLatent + 16u * g : kOOB;
-        dma16(rs_rows, voff, lds_addr(rope_ring + (i % F::kRopeST) * F::kRopeSlot + wid * F::kRopePortion));
-      }
       const uint32_t vm = (uint32_t)__ballot(ok && g == 0) & 0xFFFFu;
       if (ln == 0) sm.vmask[i % kST][wid] = vm;
+      return RowDma{base, ok, i};
+    };
+    auto row_dma = [&](const RowDma& rd, int d, int ln) {
+      const int g = ln >> 4;
+      if (d < F::kLoads) {
+        const int piece = 4 * d + g;
+        const uint32_t voff = rd.ok ? rd.base + 16u * piece : kOOB;
+        const uint32_t lds0 = lds_addr(ring + (rd.slot % kST) * F::kSlot + wid * F::kPortion);
+        if (4 * d + 3 < F::kPieces || piece < F::kPieces) dma16(rs_rows, voff, lds0 + 1024u * d);
+      } else if (kFp8 && d == F::kLoads) {
+        const uint32_t voff = rd.ok ? rd.base + (uint32_t)kLatent + 16u * g : kOOB;
+        dma16(rs_rows, voff, lds_addr(rope_ring + (rd.slot % F::kRopeST) * F::kRopeSlot + wid * F::kRopePortion));
+      }
+    };
+    auto issue_rows = [&](const Cursor& cur, int i, int ln, int32_t e) {
+      const RowDma rd = prep_rows(cur, i, ln, e);
+#pragma unroll
+      for (int d = 0; d < F::kVmOps; d++) row_dma(rd, d, ln);
     };
 
     // Query registers of the wave's 16*JT heads: Q[j][k] = B operand of QK step k for head
@@ -238,6 +253,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
         const int32_t e_next = idx_entry(s + 2, ln);
         const int pp = par ^ 1;
         const int fl_prev = sm.wflag[pp][0] | sm.wflag[pp][1] | sm.wflag[pp][2] | sm.wflag[pp][3];
+        // This step's gather (rows of tile s+2, then index entries of tile s+4): the
+        // F::kVmOps + 1 DMA instructions are spread over QK^T, so that the CU's address
+        // unit takes them while the matrix work runs instead of in one burst per wave.
+        const RowDma rd = prep_rows(cr, s + 2, ln, e_next);
+        auto gather = [&](int d) {
+          if (d < F::kVmOps) row_dma(rd, d, ln);
+          else if (d == F::kVmOps) issue_idx(cx, s + 4, ln);
+        };
 
         // ---- QK^T: rows 16*MT*rg + 16m + r16 against heads 16*JT*hg + 16j + r16
         uint32_t vrow = 0;   // bit 16m + r: row 16*MT*rg + 16m + r is valid
@@ -261,6 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
           // 8g + k/2, half k%2
 #pragma unroll
           for (int kp = 0; kp < 8; kp++) {
+            gather(kp);
             u32x4 cw[MT];
 #pragma unroll
             for (int m = 0; m < MT; m++)
@@ -275,6 +299,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
               }
             }
           }
+          gather(8);
+          gather(9);
           const SMLA_LDS uint8_t* const rslot = rope_ring + (s % F::kRopeST) * F::kRopeSlot;
 #pragma unroll
           for (int m = 0; m < MT; m++) {
@@ -298,6 +324,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
           }
 #pragma unroll
           for (int kq = 0; kq < 4; kq++) {
+            gather(2 * kq);
+            gather(2 * kq + 1);
             u32x4 cw[MT];
 #pragma unroll
             for (int m = 0; m < MT; m++)
@@ -326,6 +354,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
           }
         } else {
 #pragma unroll
+          for (int d = 0; d <= F::kVmOps; d++) gather(d);
+#pragma unroll
           for (int m = 0; m < MT; m++)
 #pragma unroll
             for (int q = 0; q < 4; q++) sp[m][q] = f16x2{(f16)0.0f, (f16)0.0f};
@@ -342,10 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
           }
         }
 
-        // ---- rows of tile s+2, index entries of tile s+4 (issued behind the matrix work)
-        issue_rows(cr, s + 2, ln, e_next);
         cr.next(cpt);
-        issue_idx(cx, s + 4, ln);
         cx.next(cpt);
 
         // ---- shared references after tile s-1 of the same segment: the largest one the
