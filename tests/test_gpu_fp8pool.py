@@ -4,7 +4,7 @@ and sparse_mla_decode_fp8pool within the decode tolerance (max |out - ref| <= 2e
 max |ref|, |lse - ref| <= 1e-3, -inf exactly where the oracle has it) against
 oracle.sparse_mla_decode_fp8pool_ref: head blocks of 16, 32 and 64, several tiles with a
 ragged tail, empty and out-of-range entries, empty tokens, every kind of split; and at
-the full sizes of the 35- and 264-token workloads on sampled tokens."""
+the full sizes of the 35-, 128-, 264- and 1,024-token workloads on sampled tokens."""
 
 import json
 import os
@@ -110,7 +110,7 @@ def test_fp8pool_empty_tokens(smla):
     assert np.all(_np(out)[[2, 5]] == 0) and np.all(np.isneginf(_np(lse)[[2, 5]]))
 
 
-@pytest.mark.parametrize("cfg", [2, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])   # 3 and 5: 64-head blocks, the FP8 role-specialised kernel
 def test_fp8pool_full_size(smla, cfg):
     wl = W.WORKLOADS[cfg]
     _say(f"fp8pool config {cfg} {wl.name}: T={wl.T} H={wl.H} pool={wl.pool_rows}")
