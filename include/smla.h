@@ -162,8 +162,8 @@ SMLA_API int32_t smla_choose_num_splits(int32_t T, int32_t H, int32_t topk);
  * Workspace bytes sparse_mla_decode needs (num_splits as passed to it, 0 = automatic):
  * the partial results and counters of the batch-sized split work ("Four-bit caches make
  * room", the sizing by token batch).
- * Also an upper bound for sparse_mla_decode_fp8rows and sparse_mla_decode_fp8pool with
- * the same arguments, whose automatic split count is never larger.
+ * The same size serves sparse_mla_decode_fp8rows and sparse_mla_decode_fp8pool with the
+ * same arguments (they pick the head blocks and the automatic split count alike).
  */
 SMLA_API size_t smla_decode_workspace_bytes(int32_t T, int32_t H, int32_t topk, int32_t num_splits);
 
@@ -195,7 +195,7 @@ SMLA_API int nvfp4_stage_fp8(const void* kv_pool_dev, int64_t pool_rows, const i
  * (E4M3 -> fp16 exactly, FP16 operands, FP32 accumulation).  indices_dev only marks
  * which entries are empty.  Arguments otherwise as in sparse_mla_decode, with
  * smla_decode_workspace_bytes giving the workspace size; heads are processed in blocks of
- * 32 or 16 (never 64).
+ * 64, 32 or 16 as there.
  */
 SMLA_API int sparse_mla_decode_fp8rows(const void* q_dev, const void* staged_dev,
                               const int32_t* indices_dev, int64_t pool_rows, int32_t T, int32_t H,
@@ -221,7 +221,7 @@ SMLA_API int fp8_pack_rows(const void* src_dev, const int32_t* slots_dev, int32_
  * fp8_pack_rows; indices_dev names its rows as for sparse_mla_decode (-1 or >= pool_rows
  * = empty).  Every other argument, the result and the workspace rule are those of
  * sparse_mla_decode (smla_decode_workspace_bytes gives the size); heads are processed in
- * blocks of 32 or 16.  pool_rows * 576 may be at most 4 GiB - 4 KiB, else
+ * blocks of 64, 32 or 16 as there.  pool_rows * 576 may be at most 4 GiB - 4 KiB, else
  * SMLA_ERR_UNSUPPORTED.
  */
 SMLA_API int sparse_mla_decode_fp8pool(const void* q_dev, const void* fp8_pool_dev, int64_t pool_rows,
