@@ -21,7 +21,8 @@ from helpers import PackedRows, assert_parity, build_device_pool, pool_source_al
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-SAMPLED_TOKENS = 64     # checked tokens where the workload has more than this
+ALL_TOKENS_UP_TO = 264  # workloads of at most this many tokens are checked token by token
+SAMPLED_TOKENS = 64     # seeded tokens checked at the larger workload
 STAGED_TOKENS = 8
 
 
@@ -49,7 +50,7 @@ def _setup(smla, cfg):
 
 
 def _checked_tokens(wl, rng, n):
-    if wl.T <= n:
+    if wl.T <= max(n, ALL_TOKENS_UP_TO):
         return list(range(wl.T))
     return sorted(set([0, wl.T - 1]) | set(rng.choice(wl.T, size=n, replace=False).tolist()))
 
