@@ -396,7 +396,7 @@ SMLA_API int smla_group_union(const int32_t* idx, int32_t T, int32_t topk, int32
 
 SMLA_API size_t smla_decode_grouped_workspace_bytes(int32_t T, int32_t H, int32_t tpg, int32_t U,
                                                     int32_t num_splits) {
-  if (!grouped_shape_ok(T, H, tpg, U) || H * tpg != 4 * kHeadGroup || T == 0 || num_splits < 0) return 0;
+  if (!grouped_shape_ok(T, H, tpg, U) || (int64_t)H * tpg != 4 * kHeadGroup || T == 0 || num_splits < 0) return 0;
   const int32_t G = num_splits > 0 ? num_splits : auto_splits(false, T / tpg, 4 * kHeadGroup, U, true);
   return make_plan(T / tpg, 4 * kHeadGroup, U, G, false, true).bytes;
 }
@@ -406,7 +406,7 @@ SMLA_API int sparse_mla_decode_grouped(const void* q, const void* pool, int64_t 
                                        void* out, float* lse, int32_t num_splits, void* ws, size_t ws_bytes,
                                        void* stream) {
   if (!grouped_shape_ok(T, H, tpg, U)) return SMLA_ERR_INVALID_ARG;
-  if (H * tpg != 4 * kHeadGroup || pool_rows > (int64_t)kRowMask + 1) return SMLA_ERR_UNSUPPORTED;
+  if ((int64_t)H * tpg != 4 * kHeadGroup || pool_rows > (int64_t)kRowMask + 1) return SMLA_ERR_UNSUPPORTED;
   return run_decode(Rows::kNvfp4Pool, q, pool, pool_rows, uni, T / tpg, 4 * kHeadGroup, U, softmax_scale, out,
                     lse, num_splits, ws, ws_bytes, stream, H);
 }
