@@ -107,6 +107,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
   using S = WsShape<NH>;
   using F = WsFmt<kFp8>;
   constexpr int JT = S::JT, RG = S::RG, MT = S::MT, NJ = S::NJ;
+  // 64-head blocks score with 32x32x16 MFMAs (a scoring wave's 32 rows x 32 heads are one
+  // tile); 16-head blocks with 16x16x32
+  constexpr bool kM32 = NH == 64;
   static_assert(!kFp8 || (NH == 64 && !kGrouped), "FP8 rows: 64-head blocks, per-token lists");
   static_assert(sizeof(SmemWs<NH, kGrouped, kFp8>) <= 160 * 1024, "LDS of one CU");
   __shared__ SmemWs<NH, kGrouped, kFp8> sm;
@@ -189,18 +192,31 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
       for (int d = 0; d < F::kVmOps; d++) row_dma(rd, d, ln);
     };
 
-    // Query registers of the wave's 16*JT heads: Q[j][k] = B operand of QK step k for head
-    // 16*JT*hg + 16j + r16 (latent features 128g + 8k.., rope 512 + 16g + 8(k-16)..).
+    // Query registers of the wave's 16*JT heads.  16x16x32: Q[j][k] = B operand of QK step
+    // k for head 16*JT*hg + 16j + r16 (latent features 128g + 8k.., rope 512 + 16g +
+    // 8(k-16)..).  32x32x16: chunk c = Qc(c) is the B operand for head 32hg + (ln & 31), K
+    // half kh = ln >> 5: latent features 256kh + 8c .. +7 (c < 32), rope 512 + 32kh +
+    // 8(c - 32) .. +7 (c = 32 .. 35).
     f16x8 Q[JT][18];
+    auto Qc = [&](int c) -> f16x8& { return Q[c / 18][c % 18]; };
     auto load_q = [&](int64_t t, int ln) {
-      const int r16 = ln & 15, g = ln >> 4;
+      if constexpr (kM32) {
+        const int kh = ln >> 5;
+        const f16* base = (const f16*)A.q + ((t * A.H + head0 + 32 * hg + (ln & 31)) * kHeadDim);
 #pragma unroll
-      for (int j = 0; j < JT; j++) {
-        const f16* base = (const f16*)A.q + ((t * A.H + head0 + 16 * JT * hg + 16 * j + r16) * kHeadDim);
+        for (int c = 0; c < 32; c++) Qc(c) = *(const f16x8*)(base + 256 * kh + 8 * c);
 #pragma unroll
-        for (int k = 0; k < 16; k++) Q[j][k] = *(const f16x8*)(base + 128 * g + 8 * k);
-        Q[j][16] = *(const f16x8*)(base + kLatent + 16 * g);
-        Q[j][17] = *(const f16x8*)(base + kLatent + 16 * g + 8);
+        for (int c = 0; c < 4; c++) Qc(32 + c) = *(const f16x8*)(base + kLatent + 32 * kh + 8 * c);
+      } else {
+        const int r16 = ln & 15, g = ln >> 4;
+#pragma unroll
+        for (int j = 0; j < JT; j++) {
+          const f16* base = (const f16*)A.q + ((t * A.H + head0 + 16 * JT * hg + 16 * j + r16) * kHeadDim);
+#pragma unroll
+          for (int k = 0; k < 16; k++) Q[j][k] = *(const f16x8*)(base + 128 * g + 8 * k);
+          Q[j][16] = *(const f16x8*)(base + kLatent + 16 * g);
+          Q[j][17] = *(const f16x8*)(base + kLatent + 16 * g + 8);
+        }
       }
     };
 
@@ -227,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
     wait_vm<F::kVmOps + 1>();   // rows(0), idx(2) have landed
     __syncthreads();         // every portion of tile 0 has landed
 
-    float mq[JT];   // shared reference of head 16*JT*hg + 16j + r16
+    float mq[JT];   // shared reference of head 16*JT*hg + 16j + r16 (32x32x16: mq[0], the lane's head)
 #pragma unroll
     for (int j = 0; j < JT; j++) mq[j] = -INFINITY;
     for (int s = 0; s <= n; s++) {
@@ -266,172 +282,290 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
         uint32_t vrow = 0;   // bit 16m + r: row 16*MT*rg + 16m + r is valid
 #pragma unroll
         for (int m = 0; m < MT; m++) vrow |= sm.vmask[s % kST][MT * rg + m] << (16 * m);
-        // grouped: byte jj of mrow[m] holds the member bits of row 16*MT*rg + 16m + 4g + jj
-        uint32_t mrow[MT];
-        if constexpr (kGrouped) {
-#pragma unroll
-          for (int m = 0; m < MT; m++)
-            mrow[m] = lds_load<uint32_t>(&sm.members[s % kST][16 * MT * rg + 16 * m + 4 * g]);
-        }
-        f32x4 acc[MT][JT];
-#pragma unroll
-        for (int m = 0; m < MT; m++)
-#pragma unroll
-          for (int j = 0; j < JT; j++) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        f16x2 sp[MT][4];   // group scales of the lane's rows: sp[m][q] = groups 8g+2q, 8g+2q+1
-        if (kFp8 && vrow != 0) {
-          // FP8: K step k reads latent features 128g + 8k .. +7 of the row: 16-byte piece
-          // 8g + k/2, half k%2
-#pragma unroll
-          for (int kp = 0; kp < 8; kp++) {
-            gather(kp);
-            u32x4 cw[MT];
-#pragma unroll
-            for (int m = 0; m < MT; m++)
-              cw[m] = lds_load<u32x4>(slot + (MT * rg + m) * F::kPortion + 256 * (8 * g + kp) + 16 * r16);
-#pragma unroll
-            for (int kk = 0; kk < 2; kk++) {
-#pragma unroll
-              for (int m = 0; m < MT; m++) {
-                const f16x8 a = fp8x8(cw[m][2 * kk], cw[m][2 * kk + 1]);
-#pragma unroll
-                for (int j = 0; j < JT; j++) acc[m][j] = mfma16x16x32(a, Q[j][2 * kp + kk], acc[m][j]);
-              }
-            }
-          }
-          gather(8);
-          gather(9);
-          const SMLA_LDS uint8_t* const rslot = rope_ring + (s % F::kRopeST) * F::kRopeSlot;
-#pragma unroll
-          for (int m = 0; m < MT; m++) {
-            const u32x4 rb = lds_load<u32x4>(rslot + (MT * rg + m) * F::kRopePortion + 256 * g + 16 * r16);
-            const f16x8 r0 = fp8x8(rb.x, rb.y), r1 = fp8x8(rb.z, rb.w);
-#pragma unroll
-            for (int j = 0; j < JT; j++) {
-              acc[m][j] = mfma16x16x32(r0, Q[j][16], acc[m][j]);
-              acc[m][j] = mfma16x16x32(r1, Q[j][17], acc[m][j]);
-            }
-          }
-        } else if (!kFp8 && vrow != 0) {
-#pragma unroll
-          for (int m = 0; m < MT; m++) {
-            const SMLA_LDS uint8_t* por = slot + (MT * rg + m) * F::kPortion + 16 * r16;
-            const u32x2 scb = lds_load<u32x2>(por + 256 * (16 + (g >> 1)) + 8 * (g & 1));
-            sp[m][0] = e4m3x2<false>(scb.x);
-            sp[m][1] = e4m3x2<true>(scb.x);
-            sp[m][2] = e4m3x2<false>(scb.y);
-            sp[m][3] = e4m3x2<true>(scb.y);
-          }
-#pragma unroll
-          for (int kq = 0; kq < 4; kq++) {
-            gather(2 * kq);
-            gather(2 * kq + 1);
-            u32x4 cw[MT];
-#pragma unroll
-            for (int m = 0; m < MT; m++)
-              cw[m] = lds_load<u32x4>(slot + (MT * rg + m) * F::kPortion + 256 * (4 * g + kq) + 16 * r16);
-#pragma unroll
-            for (int kk = 0; kk < 4; kk++) {
-              const int k = 4 * kq + kk;
-#pragma unroll
-              for (int m = 0; m < MT; m++) {
-                const f16 sk = (k & 2) ? sp[m][k >> 2].y : sp[m][k >> 2].x;
-                const f16x8 a = unpack8(cw[m][kk], f16x2{sk, sk});
-#pragma unroll
-                for (int j = 0; j < JT; j++) acc[m][j] = mfma16x16x32(a, Q[j][k], acc[m][j]);
-              }
-            }
-          }
-#pragma unroll
-          for (int m = 0; m < MT; m++) {
-            const u32x4 rb = lds_load<u32x4>(slot + (MT * rg + m) * F::kPortion + 256 * (18 + g) + 16 * r16);
-            const f16x8 r0 = fp8x8(rb.x, rb.y), r1 = fp8x8(rb.z, rb.w);
-#pragma unroll
-            for (int j = 0; j < JT; j++) {
-              acc[m][j] = mfma16x16x32(r0, Q[j][16], acc[m][j]);
-              acc[m][j] = mfma16x16x32(r1, Q[j][17], acc[m][j]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int d = 0; d <= F::kVmOps; d++) gather(d);
-#pragma unroll
-          for (int m = 0; m < MT; m++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) sp[m][q] = f16x2{(f16)0.0f, (f16)0.0f};
-        }
-        // PV scale table: the head-group-0 waves write their rows' scales (an empty row was
-        // fetched as zeros, so its scales are 0)
-        if (!kFp8 && hg == 0) {
-#pragma unroll
-          for (int m = 0; m < MT; m++) {
-            const int row = 16 * MT * rg + 16 * m + r16;
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++)
-              sm.sc[par][8 * g + jj][row] = (jj & 1) ? sp[m][jj >> 1].y : sp[m][jj >> 1].x;
-          }
-        }
-
-        cr.next(cpt);
-        cx.next(cpt);
-
-        // ---- shared references after tile s-1 of the same segment: the largest one the
-        // row groups used
-        if (s > 0 && !new_seg) {
-          if (fl_prev & 1) {
-#pragma unroll
-            for (int j = 0; j < JT; j++) {
-              const int h = 16 * JT * hg + 16 * j + r16;
-              float m = sm.wref[pp][0][h];
-#pragma unroll
-              for (int q = 1; q < RG; q++) m = fmaxf(m, sm.wref[pp][q][h]);
-              mq[j] = m;
-            }
-          }
-        }
-
-        // ---- softmax.  acc[m][j][jj] = score of row 16*MT*rg + 16m + 4g + jj, head
-        // 16*JT*hg + 16j + r16.
-        // Scores enter as exp2(score * scale_log2 - ref) in one fma each; an invalid row
-        // enters as -inf (exp2 gives 0), and a head with no valid row takes 0 for -ref.
-        // When every row of the wave is valid (and no member bits apply) no mask is needed.
-        const bool all_valid = !kGrouped && vrow == (MT == 2 ? 0xFFFFFFFFu : 0xFFFFu);
         bool raised = false;
+        if constexpr (kM32) {
+          // 32x32x16 MFMAs.  Lane (row 32rg + (ln & 31), K half kh = ln >> 5) supplies the A
+          // operand of chunk c: eight latent values 256kh + 8c .. +7 of one scale group (c <
+          // 32), or rope values 32kh + 8(c - 32) .. +7 (c = 32 .. 35).  Accumulator element i
+          // is the score of row 8(i/4) + 4kh + i%4 of the wave's 32 against head 32hg + (ln & 31).
+          const int row = ln & 31, kh = ln >> 5;
+          const int hl = 32 * hg + row;   // the lane's head in the block
+          uint32_t mrow4[4];              // grouped: member bytes of rows 8b + 4kh .. +3
+          if constexpr (kGrouped) {
 #pragma unroll
-        for (int j = 0; j < JT; j++) {
-          float sv[MT][4];
-          // grouped: the token (within the group) of heads 16*JT*hg + 16j ..
-          const int tok = kGrouped ? (16 * JT * hg + 16 * j) / A.tok_heads : 0;
+            for (int b = 0; b < 4; b++)
+              mrow4[b] = lds_load<uint32_t>(&sm.members[s % kST][32 * rg + 8 * b + 4 * kh]);
+          }
+          f32x16 acc = f32x16{};
+          f16x2 sp[8];   // NVFP4 group scales of the lane's row: sp[i] = groups 16kh + 2i, +1
+          const SMLA_LDS uint8_t* const por = slot + (2 * rg + (row >> 4)) * F::kPortion + 16 * (row & 15);
+          if (kFp8 && vrow != 0) {
+            // FP8: chunk c of half kh is bytes 256kh + 8c .. +7, piece 16kh + c/2
 #pragma unroll
-          for (int m = 0; m < MT; m++)
+            for (int pc = 0; pc < 16; pc++) {
+              gather(pc);
+              const u32x4 cw = lds_load<u32x4>(por + 256 * (16 * kh + pc));
+              acc = mfma32x32x16(fp8x8(cw.x, cw.y), Qc(2 * pc), acc);
+              acc = mfma32x32x16(fp8x8(cw.z, cw.w), Qc(2 * pc + 1), acc);
+            }
+            const SMLA_LDS uint8_t* const rpor = rope_ring + (s % F::kRopeST) * F::kRopeSlot +
+                                                 (2 * rg + (row >> 4)) * F::kRopePortion + 16 * (row & 15);
+            const u32x4 r0 = lds_load<u32x4>(rpor + 256 * (2 * kh)), r1 = lds_load<u32x4>(rpor + 256 * (2 * kh + 1));
+            acc = mfma32x32x16(fp8x8(r0.x, r0.y), Qc(32), acc);
+            acc = mfma32x32x16(fp8x8(r0.z, r0.w), Qc(33), acc);
+            acc = mfma32x32x16(fp8x8(r1.x, r1.y), Qc(34), acc);
+            acc = mfma32x32x16(fp8x8(r1.z, r1.w), Qc(35), acc);
+          } else if (!kFp8 && vrow != 0) {
+            // NVFP4: the half row's 16 group scales are scale bytes 16kh .. 16kh+15 (piece
+            // 16 + kh); its codes are pieces 8kh .. 8kh+7 (four chunks each); its rope is
+            // pieces 18 + 2kh and 19 + 2kh
+            const u32x4 scb = lds_load<u32x4>(por + 256 * (16 + kh));
+            sp[0] = e4m3x2<false>(scb.x);
+            sp[1] = e4m3x2<true>(scb.x);
+            sp[2] = e4m3x2<false>(scb.y);
+            sp[3] = e4m3x2<true>(scb.y);
+            sp[4] = e4m3x2<false>(scb.z);
+            sp[5] = e4m3x2<true>(scb.z);
+            sp[6] = e4m3x2<false>(scb.w);
+            sp[7] = e4m3x2<true>(scb.w);
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-              if (all_valid) {
-                sv[m][jj] = acc[m][j][jj];
-              } else {
-                bool valid = (vrow >> (16 * m + 4 * g + jj)) & 1;
-                if constexpr (kGrouped) valid = valid && ((mrow[m] >> (8 * jj + tok)) & 1);
-                sv[m][jj] = valid ? acc[m][j][jj] : -INFINITY;
+            for (int q = 0; q < 8; q++) {
+              gather(q);
+              const u32x4 cw = lds_load<u32x4>(por + 256 * (8 * kh + q));
+#pragma unroll
+              for (int kk = 0; kk < 4; kk++) {
+                const int c = 4 * q + kk;   // group 16kh + c/2
+                const f16 sk = ((c >> 1) & 1) ? sp[c >> 2].y : sp[c >> 2].x;
+                acc = mfma32x32x16(unpack8(cw[kk], f16x2{sk, sk}), Qc(c), acc);
               }
             }
-          float mx = sv[0][0];
+            const u32x4 r0 = lds_load<u32x4>(por + 256 * (18 + 2 * kh)), r1 = lds_load<u32x4>(por + 256 * (19 + 2 * kh));
+            acc = mfma32x32x16(fp8x8(r0.x, r0.y), Qc(32), acc);
+            acc = mfma32x32x16(fp8x8(r0.z, r0.w), Qc(33), acc);
+            acc = mfma32x32x16(fp8x8(r1.x, r1.y), Qc(34), acc);
+            acc = mfma32x32x16(fp8x8(r1.z, r1.w), Qc(35), acc);
+          } else {
+#pragma unroll
+            for (int d = 0; d <= F::kVmOps; d++) gather(d);
+#pragma unroll
+            for (int i = 0; i < 8; i++) sp[i] = f16x2{(f16)0.0f, (f16)0.0f};
+          }
+          // PV scale table: the head-group-0 waves write their rows' scales (an empty row was
+          // fetched as zeros, so its scales are 0)
+          if (!kFp8 && hg == 0) {
+#pragma unroll
+            for (int jj = 0; jj < 16; jj++)
+              sm.sc[par][16 * kh + jj][32 * rg + row] = (jj & 1) ? sp[jj >> 1].y : sp[jj >> 1].x;
+          }
+
+          cr.next(cpt);
+          cx.next(cpt);
+
+          // ---- shared reference of the lane's head after tile s-1 of the same segment: the
+          // largest one the row groups used
+          if (s > 0 && !new_seg && (fl_prev & 1)) {
+            float m = sm.wref[pp][0][hl];
+#pragma unroll
+            for (int q = 1; q < RG; q++) m = fmaxf(m, sm.wref[pp][q][hl]);
+            mq[0] = m;
+          }
+
+          // ---- softmax over the lane's 16 rows and its partner lane's (ln ^ 32) 16, as below
+          const bool all_valid = !kGrouped && vrow == 0xFFFFFFFFu;
+          const int tok = kGrouped ? hl / A.tok_heads : 0;
+          float sv[16];
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            if (all_valid) {
+              sv[i] = acc[i];
+            } else {
+              bool valid = (vrow >> (8 * (i >> 2) + 4 * kh + (i & 3))) & 1;
+              if constexpr (kGrouped) valid = valid && ((mrow4[i >> 2] >> (8 * (i & 3) + tok)) & 1);
+              sv[i] = valid ? acc[i] : -INFINITY;
+            }
+          }
+          float mx = sv[0];
+#pragma unroll
+          for (int i = 1; i < 16; i++) mx = fmaxf(mx, sv[i]);
+          mx = wave_max_xor32(mx * sl2);   // scale_log2 > 0: the scaled maximum
+          const float ref = (mx > mq[0] + kSlack) ? mx : mq[0];
+          raised = ref != mq[0];
+          const float nref = (ref == -INFINITY) ? 0.0f : -ref;
+#pragma unroll
+          for (int b = 0; b < 4; b++) {
+            f16 pr[4];
+#pragma unroll
+            for (int ii = 0; ii < 4; ii++) pr[ii] = (f16)__builtin_amdgcn_exp2f(fmaf(sv[4 * b + ii], sl2, nref));
+            lds_store<f16x4>(&sm.pb[par][hl][32 * rg + 8 * b + 4 * kh], f16x4{pr[0], pr[1], pr[2], pr[3]});
+          }
+          sm.wref[par][rg][hl] = ref;
+        } else {
+          // grouped: byte jj of mrow[m] holds the member bits of row 16*MT*rg + 16m + 4g + jj
+          uint32_t mrow[MT];
+          if constexpr (kGrouped) {
+#pragma unroll
+            for (int m = 0; m < MT; m++)
+              mrow[m] = lds_load<uint32_t>(&sm.members[s % kST][16 * MT * rg + 16 * m + 4 * g]);
+          }
+          f32x4 acc[MT][JT];
 #pragma unroll
           for (int m = 0; m < MT; m++)
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++) mx = fmaxf(mx, sv[m][jj]);
-          mx = wave_max_xor16_32(mx * sl2);   // scale_log2 > 0: the scaled maximum
-          const float ref = (mx > mq[j] + kSlack) ? mx : mq[j];
-          raised |= ref != mq[j];
-          const float nref = (ref == -INFINITY) ? 0.0f : -ref;
-          const int h = 16 * JT * hg + 16 * j + r16;
+            for (int j = 0; j < JT; j++) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          f16x2 sp[MT][4];   // group scales of the lane's rows: sp[m][q] = groups 8g+2q, 8g+2q+1
+          if (kFp8 && vrow != 0) {
+            // FP8: K step k reads latent features 128g + 8k .. +7 of the row: 16-byte piece
+            // 8g + k/2, half k%2
 #pragma unroll
-          for (int m = 0; m < MT; m++) {
-            f16 p[4];
+            for (int kp = 0; kp < 8; kp++) {
+              gather(kp);
+              u32x4 cw[MT];
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++) p[jj] = (f16)__builtin_amdgcn_exp2f(fmaf(sv[m][jj], sl2, nref));
-            lds_store<f16x4>(&sm.pb[par][h][16 * MT * rg + 16 * m + 4 * g], f16x4{p[0], p[1], p[2], p[3]});
+              for (int m = 0; m < MT; m++)
+                cw[m] = lds_load<u32x4>(slot + (MT * rg + m) * F::kPortion + 256 * (8 * g + kp) + 16 * r16);
+#pragma unroll
+              for (int kk = 0; kk < 2; kk++) {
+#pragma unroll
+                for (int m = 0; m < MT; m++) {
+                  const f16x8 a = fp8x8(cw[m][2 * kk], cw[m][2 * kk + 1]);
+#pragma unroll
+                  for (int j = 0; j < JT; j++) acc[m][j] = mfma16x16x32(a, Q[j][2 * kp + kk], acc[m][j]);
+                }
+              }
+            }
+            gather(8);
+            gather(9);
+            const SMLA_LDS uint8_t* const rslot = rope_ring + (s % F::kRopeST) * F::kRopeSlot;
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+              const u32x4 rb = lds_load<u32x4>(rslot + (MT * rg + m) * F::kRopePortion + 256 * g + 16 * r16);
+              const f16x8 r0 = fp8x8(rb.x, rb.y), r1 = fp8x8(rb.z, rb.w);
+#pragma unroll
+              for (int j = 0; j < JT; j++) {
+                acc[m][j] = mfma16x16x32(r0, Q[j][16], acc[m][j]);
+                acc[m][j] = mfma16x16x32(r1, Q[j][17], acc[m][j]);
+              }
+            }
+          } else if (!kFp8 && vrow != 0) {
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+              const SMLA_LDS uint8_t* por = slot + (MT * rg + m) * F::kPortion + 16 * r16;
+              const u32x2 scb = lds_load<u32x2>(por + 256 * (16 + (g >> 1)) + 8 * (g & 1));
+              sp[m][0] = e4m3x2<false>(scb.x);
+              sp[m][1] = e4m3x2<true>(scb.x);
+              sp[m][2] = e4m3x2<false>(scb.y);
+              sp[m][3] = e4m3x2<true>(scb.y);
+            }
+#pragma unroll
+            for (int kq = 0; kq < 4; kq++) {
+              gather(2 * kq);
+              gather(2 * kq + 1);
+              u32x4 cw[MT];
+#pragma unroll
+              for (int m = 0; m < MT; m++)
+                cw[m] = lds_load<u32x4>(slot + (MT * rg + m) * F::kPortion + 256 * (4 * g + kq) + 16 * r16);
+#pragma unroll
+              for (int kk = 0; kk < 4; kk++) {
+                const int k = 4 * kq + kk;
+#pragma unroll
+                for (int m = 0; m < MT; m++) {
+                  const f16 sk = (k & 2) ? sp[m][k >> 2].y : sp[m][k >> 2].x;
+                  const f16x8 a = unpack8(cw[m][kk], f16x2{sk, sk});
+#pragma unroll
+                  for (int j = 0; j < JT; j++) acc[m][j] = mfma16x16x32(a, Q[j][k], acc[m][j]);
+                }
+              }
+            }
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+              const u32x4 rb = lds_load<u32x4>(slot + (MT * rg + m) * F::kPortion + 256 * (18 + g) + 16 * r16);
+              const f16x8 r0 = fp8x8(rb.x, rb.y), r1 = fp8x8(rb.z, rb.w);
+#pragma unroll
+              for (int j = 0; j < JT; j++) {
+                acc[m][j] = mfma16x16x32(r0, Q[j][16], acc[m][j]);
+                acc[m][j] = mfma16x16x32(r1, Q[j][17], acc[m][j]);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int d = 0; d <= F::kVmOps; d++) gather(d);
+#pragma unroll
+            for (int m = 0; m < MT; m++)
+#pragma unroll
+              for (int q = 0; q < 4; q++) sp[m][q] = f16x2{(f16)0.0f, (f16)0.0f};
           }
-          sm.wref[par][rg][h] = ref;
+          // PV scale table: the head-group-0 waves write their rows' scales (an empty row was
+          // fetched as zeros, so its scales are 0)
+          if (!kFp8 && hg == 0) {
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+              const int row = 16 * MT * rg + 16 * m + r16;
+#pragma unroll
+              for (int jj = 0; jj < 8; jj++)
+                sm.sc[par][8 * g + jj][row] = (jj & 1) ? sp[m][jj >> 1].y : sp[m][jj >> 1].x;
+            }
+          }
+
+          cr.next(cpt);
+          cx.next(cpt);
+
+          // ---- shared references after tile s-1 of the same segment: the largest one the
+          // row groups used
+          if (s > 0 && !new_seg) {
+            if (fl_prev & 1) {
+#pragma unroll
+              for (int j = 0; j < JT; j++) {
+                const int h = 16 * JT * hg + 16 * j + r16;
+                float m = sm.wref[pp][0][h];
+#pragma unroll
+                for (int q = 1; q < RG; q++) m = fmaxf(m, sm.wref[pp][q][h]);
+                mq[j] = m;
+              }
+            }
+          }
+
+          // ---- softmax.  acc[m][j][jj] = score of row 16*MT*rg + 16m + 4g + jj, head
+          // 16*JT*hg + 16j + r16.
+          // Scores enter as exp2(score * scale_log2 - ref) in one fma each; an invalid row
+          // enters as -inf (exp2 gives 0), and a head with no valid row takes 0 for -ref.
+          // When every row of the wave is valid (and no member bits apply) no mask is needed.
+          const bool all_valid = !kGrouped && vrow == (MT == 2 ? 0xFFFFFFFFu : 0xFFFFu);
+#pragma unroll
+          for (int j = 0; j < JT; j++) {
+            float sv[MT][4];
+            // grouped: the token (within the group) of heads 16*JT*hg + 16j ..
+            const int tok = kGrouped ? (16 * JT * hg + 16 * j) / A.tok_heads : 0;
+#pragma unroll
+            for (int m = 0; m < MT; m++)
+#pragma unroll
+              for (int jj = 0; jj < 4; jj++) {
+                if (all_valid) {
+                  sv[m][jj] = acc[m][j][jj];
+                } else {
+                  bool valid = (vrow >> (16 * m + 4 * g + jj)) & 1;
+                  if constexpr (kGrouped) valid = valid && ((mrow[m] >> (8 * jj + tok)) & 1);
+                  sv[m][jj] = valid ? acc[m][j][jj] : -INFINITY;
+                }
+              }
+            float mx = sv[0][0];
+#pragma unroll
+            for (int m = 0; m < MT; m++)
+#pragma unroll
+              for (int jj = 0; jj < 4; jj++) mx = fmaxf(mx, sv[m][jj]);
+            mx = wave_max_xor16_32(mx * sl2);   // scale_log2 > 0: the scaled maximum
+            const float ref = (mx > mq[j] + kSlack) ? mx : mq[j];
+            raised |= ref != mq[j];
+            const float nref = (ref == -INFINITY) ? 0.0f : -ref;
+            const int h = 16 * JT * hg + 16 * j + r16;
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+              f16 p[4];
+#pragma unroll
+              for (int jj = 0; jj < 4; jj++) p[jj] = (f16)__builtin_amdgcn_exp2f(fmaf(sv[m][jj], sl2, nref));
+              lds_store<f16x4>(&sm.pb[par][h][16 * MT * rg + 16 * m + 4 * g], f16x4{p[0], p[1], p[2], p[3]});
+            }
+            sm.wref[par][rg][h] = ref;
+          }
         }
         const bool wave_raised = __ballot(raised) != 0;
         sm.wflag[par][wid] = (wave_raised ? 1 : 0) | (vrow != 0 ? 2 : 0);
