@@ -20,9 +20,9 @@
 //    without a memory access; index entries run two tiles ahead of the rows.
 //  * QK^T: the scoring waves cover the tile's 64 rows x NH heads as RG row groups x HW head
 //    groups; scoring wave w takes row group w % RG (MT tiles of 16 rows) and head group
-//    w / RG (JT tiles of 16 heads).  Per K step it unpacks MT row fragments (A operands)
-//    and issues MT*JT MFMAs against its JT query fragments.  NH = 64: 32 rows x 32 heads
-//    per wave (each row unpacked by two waves); NH = 16: 16 rows x 16 heads.
+//    w / RG (JT tiles of 16 heads).  NH = 64: 32 rows x 32 heads per wave (each row
+//    unpacked by two waves) as one v_mfma_f32_32x32x16_f16 tile, each 16-byte ring read
+//    feeding four MFMAs; NH = 16: 16 rows x 16 heads on v_mfma_f32_16x16x32_f16.
 //  * Softmax per head over the tile's 64 rows, shared between the row groups through a
 //    per-head reference in LDS (a row group keeps the shared reference unless its rows
 //    exceed it by more than the slack); probabilities and the rows' group scales to LDS.
