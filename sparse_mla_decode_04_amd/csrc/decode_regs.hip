@@ -42,6 +42,7 @@ struct __attribute__((aligned(16))) SmemR {
   float wref[2][kWaves][kHeadGroup];        // reference each wave used [parity][wave][head]
   int wflag[2][kWaves];                     // bit 0: wave raised a reference; bit 1: wave has a row
   int flag;
+  int early_last;                           // kEarly: the early count of the first token completed it
 };
 static_assert(sizeof(SmemR) <= 81920, "two workgroups per CU");
 
@@ -64,6 +65,10 @@ __device__ __forceinline__ int32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 
 }  // namespace
 
+// kEarly (stream-K ranges that cross tokens): a range counts itself for its first token as
+// soon as that token's part ends (below).  Without it (ranges inside one token, where the
+// first token is the range's only one) the loop carries no code for it.
+template <bool kEarly>
 __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeArgs A) {
   constexpr int NH = kHeadGroup;
   __shared__ SmemR sm;
@@ -288,6 +293,19 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   cu.init(c_lo, cpt);
   const int64_t t_first = cu.t;
   int64_t pend_t[2] = {-1, -1};   // tokens this range wrote partials for (first, last)
+  // Early count of the first token (kEarly).  A range that starts inside a token finishes
+  // that token's part in its first tiles, while the range before it finishes the token at
+  // its end; counted at the end of both, the token is merged by whichever ends later, and a
+  // range can end up merging two tokens one after the other.  So when the first token's
+  // segment ends three or more iterations before the range's last, the range counts itself
+  // for it at once: its partial's stores (issued at the end of iteration e - 1) have completed
+  // at the end of iteration e, where at most that iteration's 7 loads (6 row pieces and an
+  // index entry) are left in flight -- no query DMA or segment end falls there while a token
+  // spans four or more tiles; the barrier orders every wave's stores, and thread 0 counts in
+  // iteration e + 1, using the counter's value only at that iteration's end.  The range
+  // then merges the token only if its count completed it.
+  int early_wait = -1;   // iteration e, or -1
+  int64_t early_t = -1;
   // ---- end of a token segment after tile cu: write the output or a partial, start afresh
   auto segment_end = [&](int i) {
     if (i == n - 1 || cu.ci == cpt - 1) {
@@ -297,7 +315,14 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
       const int seg = (t == t_first) ? 0 : 1;
       finish_segment<1>(A, O, m_ref, l_acc, t, full, ((int64_t)hb * G + w) * 2 + seg, head0, wid, g, r16,
                         ws_o, ws_l);
-      if (!full) pend_t[seg] = t;
+      if (!full) {
+        if (kEarly && seg == 0 && cpt >= 4 && i <= n - 4) {
+          early_wait = i + 2;
+          early_t = t;
+        } else {
+          pend_t[seg] = t;
+        }
+      }
     }
     cu.next(cpt);
   };
@@ -379,6 +404,9 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
   for (int i = 1; i < n; i++) {
     const int par = i & 1, ppar = par ^ 1;
     const bool new_seg = cu.ci == cpt - 1;   // tile i starts a later token
+    int early_old = 0;
+    if (kEarly && i == early_wait + 1 && tid == 0)
+      early_old = atomicAdd(A.counters + (int64_t)hb * A.T + early_t, 1);
     if (new_seg) new_token_q(cu.t + 1, Q);
     stage_q(i);
     f16x8 bop[2];
@@ -400,6 +428,16 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
     pv(ppar, bop);
     __builtin_amdgcn_s_setprio(0);
     segment_end(i - 1);
+    if constexpr (kEarly) {
+      if (i == early_wait) wait_vm<kRowLoads + 1>();   // the first token's partial has been written
+      if (i == early_wait + 1 && tid == 0) {
+        const int64_t tok0 = early_t * cpt;
+        const int others = (int)(wg_of_chunk(tok0 + cpt - 1, C, G) - wg_of_chunk(tok0, C, G));
+        const int last = early_old == others;
+        if (last) atomicExch(A.counters + (int64_t)hb * A.T + early_t, 0);
+        sm.early_last = last;
+      }
+    }
     __syncthreads();
   }
 
@@ -414,11 +452,20 @@ __global__ __launch_bounds__(256, 2) void sparse_mla_decode_regs_kernel(DecodeAr
 
   // ---- publish this range's partials and merge the tokens whose last range this is (the
   // code slots are idle from here on and serve as the merge's scratch)
-  publish_and_merge<NH>(A, pend_t, hb, head0, ws_o, ws_l, &sm.flag, (float*)sm.codes);
+  int counted = 0;
+  if (kEarly && early_wait >= 0) {   // counted in iteration early_wait + 1 < n; the loop's barriers order it
+    if (sm.early_last) pend_t[0] = early_t;
+    counted = 1;
+  }
+  publish_and_merge<NH>(A, pend_t, hb, head0, ws_o, ws_l, &sm.flag, (float*)sm.codes, counted);
 }
 
 hipError_t launch_decode_nvfp4_regs(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(sparse_mla_decode_regs_kernel, dim3(a.G * a.HB), dim3(256), 0, s, a);
+  // ranges inside one token (G a multiple of T) never take the early count
+  if (a.T > 0 && a.G % a.T == 0)
+    hipLaunchKernelGGL(sparse_mla_decode_regs_kernel<false>, dim3(a.G * a.HB), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(sparse_mla_decode_regs_kernel<true>, dim3(a.G * a.HB), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

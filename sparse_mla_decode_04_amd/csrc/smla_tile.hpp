@@ -200,10 +200,13 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& A, f32x4 (&O)[N
 // then one counter increment per pending token) and, for each token whose last range this
 // is, merge the token's partials into out / lse.  pend_t[seg] is the token this range wrote
 // partial slot seg for, or -1.  flag: one int of LDS; scratch: >= 2048 floats of idle LDS.
+// Bit seg of `counted`: the range counted itself for token pend_t[seg] earlier and found it
+// was the last (pend_t[seg] is -1 if it was not): merge without counting again.
 template <int NH>
 __device__ __forceinline__ void publish_and_merge(const DecodeArgs& A, const int64_t (&pend_t)[2], int hb, int head0,
                                                   __amdgpu_buffer_rsrc_t ws_o,
-                                                  __amdgpu_buffer_rsrc_t ws_l, int* flag, float* scratch) {
+                                                  __amdgpu_buffer_rsrc_t ws_l, int* flag, float* scratch,
+                                                  int counted = 0) {
   const int64_t C = A.tiles;
   const int G = A.G;
   const int cpt = A.cpt;
@@ -217,10 +220,13 @@ __device__ __forceinline__ void publish_and_merge(const DecodeArgs& A, const int
     const int64_t tok0 = t * cpt;
     const int64_t w_lo = wg_of_chunk(tok0, C, G), w_hi = wg_of_chunk(tok0 + cpt - 1, C, G);
     if (tid == 0) {
-      int32_t* cnt = A.counters + (int64_t)hb * A.T + t;
-      const int old = atomicAdd(cnt, 1);
-      const int last = (old == (int)(w_hi - w_lo));
-      if (last) atomicExch(cnt, 0);
+      int last = 1;
+      if (!((counted >> seg) & 1)) {
+        int32_t* cnt = A.counters + (int64_t)hb * A.T + t;
+        const int old = atomicAdd(cnt, 1);
+        last = (old == (int)(w_hi - w_lo));
+        if (last) atomicExch(cnt, 0);
+      }
       *flag = last;
     }
     __syncthreads();

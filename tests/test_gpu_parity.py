@@ -293,6 +293,47 @@ def test_workspace_is_left_clean_for_reuse(smla):
     assert np.all(cnt == 0)
 
 
+def _early_count_ranges(T, K, G):
+    """Ranges that start inside a token of four or more tiles and finish their part of it three
+    or more tiles before their own end: (range, tiles, tiles to the part's end) for each.
+    Range w covers tiles [w*C // G, (w+1)*C // G) of the T*cpt tiles."""
+    cpt = -(-K // 64)
+    C = T * cpt
+    out = []
+    for w in range(G):
+        lo, hi = w * C // G, (w + 1) * C // G
+        t = lo // cpt
+        first_end = min(hi - lo, (t + 1) * cpt - lo)
+        starts_inside = lo > t * cpt or hi < (t + 1) * cpt
+        if cpt >= 4 and starts_inside and first_end <= hi - lo - 3:
+            out.append((w, hi - lo, first_end))
+    return out
+
+
+@pytest.mark.parametrize("T,H,K,splits", [(9, 16, 250, 7), (9, 16, 250, 8), (9, 48, 250, 10),
+                                          (11, 16, 200, 12), (7, 16, 1000, 25)])
+def test_decode_ranges_that_count_their_first_token_early(smla, T, H, K, splits):
+    # Stream-K split counts (not a multiple of T) under which a range that starts inside a token
+    # counts itself for that token while it still has tiles of the next: four tiles per token
+    # with a ragged last tile, and a range whose first part ends exactly three tiles before its
+    # last.  Repeated launches on one workspace also check that the counters return to zero.
+    early = _early_count_ranges(T, K, splits)
+    assert splits % T != 0 and any(n - e == 3 for _, n, e in early), early
+    _say("early count", T, H, K, splits, early)
+    wl, src, q, idx = _setup(T, H, 7000, K, 0.1, 31 + splits)
+    pool = build_device_pool(src, DEV)
+    ref_out, ref_lse = oracle.sparse_mla_decode_ref(q, OracleRows(src), idx, wl.softmax_scale)
+    ws = smla.make_workspace(T, H, K, splits, DEV)
+    qd, idd = torch.from_numpy(q).to(DEV), torch.from_numpy(idx).to(DEV)
+    for rep in range(3):
+        out, lse = smla.sparse_mla_decode(qd, pool, idd, wl.softmax_scale, num_splits=splits, workspace=ws)
+        assert_parity(_np(out), _np(lse), ref_out, ref_lse, f"early count splits {splits} rep {rep}")
+    from sparse_mla_decode_04_amd.binding import decode_workspace_bytes
+    nb = decode_workspace_bytes(T, H, K, splits)
+    cnt = _np(ws[nb - 256:nb - 256 + 4 * T * (H // 16)]).view(np.int32)
+    assert np.all(cnt == 0)
+
+
 # ----------------------------------------------------------------------------- combine
 
 def test_combine_matches_oracle(smla):
