@@ -350,12 +350,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_decode_ws_kernel(Decod
 #pragma unroll
             for (int i = 0; i < 8; i++) sp[i] = f16x2{(f16)0.0f, (f16)0.0f};
           }
-          // PV scale table: the head-group-0 waves write their rows' scales (an empty row was
-          // fetched as zeros, so its scales are 0)
-          if (!kFp8 && hg == 0) {
+          // PV scale table: both waves of a row group hold its rows' scales; head group hg
+          // writes groups 16kh + 8hg .. +7 (an empty row was fetched as zeros, so its scales
+          // are 0), picking its half of the registers by a select, not a branch.
+          if constexpr (!kFp8) {
 #pragma unroll
-            for (int jj = 0; jj < 16; jj++)
-              sm.sc[par][16 * kh + jj][32 * rg + row] = (jj & 1) ? sp[jj >> 1].y : sp[jj >> 1].x;
+            for (int jj = 0; jj < 8; jj++) {
+              const f16x2 v = hg ? sp[4 + (jj >> 1)] : sp[jj >> 1];
+              sm.sc[par][16 * kh + 8 * hg + jj][32 * rg + row] = (jj & 1) ? v.y : v.x;
+            }
           }
 
           cr.next(cpt);
