@@ -57,7 +57,8 @@ def _compile(src, extra):
         m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
         if m and int(m.group(1)) > 0:
             raise RuntimeError(f"{src}: kernel {kernel} spills to scratch ({m.group(1)} bytes/lane)")
-        if "remark:" not in line and not re.match(r"^\s*(\d+\s*)?\|", line) and line.strip() != "^":
+        if ("remark:" not in line and not line.startswith("In file included from")
+                and not re.match(r"^\s*(\d+\s*)?\|", line) and line.strip() != "^"):
             remarks.append(line)
     return obj, "\n".join(remarks)
 
