@@ -17,9 +17,6 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsmla.so")
 SOURCES = ["codec.hip", "decode.hip", "decode_regs.hip", "decode_ws.hip", "group.hip", "indexer.hip", "layout.hip", "api.hip"]
-# per-source flags: the 64-head kernel keeps its 128-value accumulator in the MFMA
-# accumulation registers, so it is built without the VGPR-only MFMA form
-NO_VGPR_FORM = {"decode_ws.hip"}
 ARCH = "gfx950"
 
 FLAGS = [
@@ -42,8 +39,7 @@ def _hipcc():
 
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    flags = [f for f in FLAGS if src not in NO_VGPR_FORM or f not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
-    cmd = [_hipcc(), *flags, "-Rpass-analysis=kernel-resource-usage", *extra, "-c",
+    cmd = [_hipcc(), *FLAGS, "-Rpass-analysis=kernel-resource-usage", *extra, "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
